@@ -1,0 +1,144 @@
+/*
+ * wq.h -- C ABI of libwq.so: weight-only low-bit dequantize-and-multiply on AMD MI355X (gfx950).
+ *
+ * What the library computes (sources are the web pages the method is described on):
+ *   - Weights are stored offline as packed low-bit codes and decoded in real time to BF16,
+ *     the arithmetic being carried out on BF16 values with fp32 accumulation
+ *     (FastDeploy "WINT2 Quantization", opening paragraph).
+ *   - Formats:
+ *       WQ_FMT_INT4         two signed 4-bit codes per byte, the first in the low nibble,
+ *                           sign-extended (coursefy lesson E6.4 "GPTQ and AWQ", "Do it in
+ *                           code"); x_hat = s * q with a bf16 scale per group of 64 along k,
+ *                           or per output channel (group = 0).
+ *       WQ_FMT_INT2_AFFINE  plain 2-bit codes, four per byte, lowest two bits first;
+ *                           x_hat = s * (q - z) (lesson E6.4, "Math and notation") with a bf16
+ *                           scale and a u8 zero point per group of 64.
+ *       WQ_FMT_CCQ2         convolutional-code quantization (L,N,S) = (6,4,3) with code
+ *                           cluster, one byte per 4 weights ("CCQ: Convolutional Code for
+ *                           Extreme Low-bit Quantization in LLMs", section 3.3 and section 3.5,
+ *                           algorithm "Dequantization with Code Cluster", table of dequantization
+ *                           configurations).  Per weight:
+ *                             C  = clamp(round_half_even(fmaf(C', code_scale, code_zero)), 0, 32767)
+ *                             u  = (C >> (9 - 3*(k%4))) & 0x3F
+ *                             s  = f32(s_q) * super_scale           (s_q: 4-bit group scale)
+ *                             x_hat = bf16(f32(u - zp) * s)
+ *
+ * Layouts (every matrix is W[n][k], k contiguous, y = x W^T; an MoE tensor adds a leading
+ * expert dimension; group = 64 along k; G = k / 64):
+ *   INT4:   codes u8[E][n][k/2]; scales bf16[E][n][G] (group 64) or bf16[E][n] (group 0).
+ *   AFFINE: codes u8[E][n][k/4]; scales bf16[E][n][G]; zeros u8[E][n][G].
+ *   CCQ2:   codes u8[E][n][k/4]; qscale u8[E][n][(G+1)/2], two 4-bit group scales per byte,
+ *           the even group in the low nibble; super_scale, code_scale, code_zero f32[E][n];
+ *           zp (32 for the symmetric 6-bit states).
+ *
+ * Conventions for every call below:
+ *   - Every pointer inside wq_weight and every tensor argument of a compute call is DEVICE
+ *     memory owned by the caller; the library never frees or retains it.  Only the
+ *     wq_weight struct itself is read on the host, during the call.
+ *   - Compute calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream)
+ *     and never synchronize the host.  The library allocates no device memory in them.
+ *   - Arguments are validated on the host before anything is launched; a negative status
+ *     means nothing was launched and no output was touched.  wq_last_error() then gives a
+ *     human-readable detail (thread-local).
+ *   - Results are deterministic: no floating-point atomics; identical calls give identical
+ *     bits.
+ *   - Scales (bf16 scales, CCQ super/code scales) must be finite and the scales non-negative;
+ *     wq_gemm / wq_moe_ffn need a CCQ zero point of 0 or a power of two (the kernels form
+ *     (u - zp) * s as fma(u, s, -zp * s), the same single rounding when zp * s is exact) and
+ *     2-bit affine zero points below 256.  The decoded weights the products use are the
+ *     same bits wq_dequantize returns.
+ *   - Sizes are element counts (int64).  Device pointers must be 16-byte aligned.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WQ_OK = 0,
+  WQ_ERR_ARG = -1,         /* null pointer, bad size or shape                         */
+  WQ_ERR_UNSUPPORTED = -2, /* format / group / size combination not supported          */
+  WQ_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned                  */
+  WQ_ERR_RANGE = -4,       /* an INT4 code outside -8..7 (wq_pack_int4)                 */
+  WQ_ERR_WORKSPACE = -5,   /* workspace smaller than wq_moe_workspace_bytes()           */
+  WQ_ERR_HIP = -6          /* the HIP runtime reported an error at launch               */
+} wq_status;
+
+typedef enum { WQ_FMT_INT4 = 1, WQ_FMT_INT2_AFFINE = 2, WQ_FMT_CCQ2 = 3 } wq_format;
+
+/* A packed weight tensor [experts][n][k] in device memory (see layouts above). */
+typedef struct {
+  int32_t format;            /* wq_format                                                  */
+  int32_t group;             /* 64, or 0 = per output channel (INT4 only)                  */
+  int64_t experts;           /* 1 for a dense matrix                                       */
+  int64_t n;                 /* output channels per expert                                 */
+  int64_t k;                 /* input channels; a multiple of 64                           */
+  const uint8_t* codes;
+  const uint16_t* scales;    /* bf16 bits; INT4 and AFFINE                                 */
+  const uint8_t* zeros;      /* AFFINE                                                     */
+  const uint8_t* qscale;     /* CCQ2                                                       */
+  const float* super_scale;  /* CCQ2                                                       */
+  const float* code_scale;   /* CCQ2                                                       */
+  const float* code_zero;    /* CCQ2                                                       */
+  int32_t zp;                /* CCQ2 weight zero point                                     */
+} wq_weight;
+
+/* Decode every weight to bf16, out[e][n][k] (device, bf16 bits).  Bit-exact with the
+ * formulas above (CCQ paper section 3.5; lesson E6.4 "Math and notation"). */
+wq_status wq_dequantize(const wq_weight* w, uint16_t* out, void* stream);
+
+/* Dense weight-only product y[m][n] = bf16(sum_k x[m][k] * x_hat[n][k]) with bf16 operands
+ * and fp32 accumulation (FastDeploy "WINT2 Quantization"; the pages' GEMV and grouped-GEMM
+ * operator benchmarks).  x bf16 [m][k], y bf16 [m][n], w->experts must be 1.  m == 0 is a
+ * no-op.  Small m (<= 32) runs the decode kernels that stream the packed weights once;
+ * larger m runs the MFMA kernel with LDS-staged dequantized tiles. */
+wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y, void* stream);
+
+/* Bytes of device workspace wq_moe_route / wq_moe_ffn need for t tokens, top-k routing over
+ * `experts` experts, hidden size `hidden` and expert intermediate size `inter`. */
+size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t hidden,
+                              int64_t inter);
+
+/* Group the (token, slot) pairs p = t*topk + j by expert (sort by expert id, stable in p):
+ * expert_offsets[e] = number of pairs routed to experts < e (expert_offsets[experts] =
+ * t*topk); sorted_pairs[expert_offsets[e] ...] lists expert e's pairs in increasing p.
+ * topk_ids int32 [t][topk] must lie in [0, experts) (not checked on the device). */
+wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t experts,
+                       int32_t* expert_offsets, int32_t* sorted_pairs, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* MoE expert FFN with routed tokens grouped per expert:
+ *   y[t] = bf16( sum_{j<topk} topk_weights[t][j] * W_down[e] h_{t,j} ),  e = topk_ids[t][j],
+ *   h_{t,j} = bf16( SiLU(W_gate[e] x_t) * (W_up[e] x_t) )
+ * x bf16 [t][hidden], y bf16 [t][hidden]; gate and up are [E][inter][hidden], down is
+ * [E][hidden][inter]; the slot sum runs in order j = 0..topk-1 in fp32.  Routing weights are
+ * used as given.  ws must hold wq_moe_workspace_bytes(t, topk, E, hidden, inter) bytes. */
+wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
+                     const float* topk_weights, int32_t topk, const wq_weight* gate,
+                     const wq_weight* up, const wq_weight* down, uint16_t* y, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Host helpers for the INT4 storage format (lesson E6.4, "Do it in code"); host memory.
+ * wq_pack_int4: two codes per byte, the first in the low nibble, an odd count padded with 0;
+ *   out must hold (n+1)/2 bytes; WQ_ERR_RANGE (nothing written) for a code outside -8..7.
+ * wq_unpack_int4: the first n codes, sign-extended; data holds at least (n+1)/2 bytes.
+ * wq_packed_size: nominal bytes of n_codes codes of `bits` bits (n*bits/8, rounded up);
+ *   -1 for negative n or bits outside 1..32. */
+wq_status wq_pack_int4(const int32_t* codes, int64_t n, uint8_t* out);
+wq_status wq_unpack_int4(const uint8_t* data, int64_t n, int32_t* out);
+int64_t wq_packed_size(int64_t n_codes, int32_t bits);
+
+/* Name of a status code, and the detail of the calling thread's last failure. */
+const char* wq_status_string(int32_t status);
+const char* wq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

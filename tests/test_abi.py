@@ -1,0 +1,134 @@
+"""CPU tests of the C ABI: the library loads and exports every symbol include/wq.h declares,
+the host helpers reproduce the pages' values, and invalid arguments are rejected on the host
+before anything is launched (none of these calls reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import weight_only_bit_amd as wq
+
+    if not os.path.exists(wq.LIB_PATH):
+        from weight_only_bit_amd import build
+
+        build.build()
+    wq.lib()
+    return wq
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "wq.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(wq):
+    names = _declared()
+    assert len(names) >= 10
+    L = wq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(wq.EXPORTS) == names
+
+
+def test_pack_helpers_match_printed_values(wq):
+    assert wq.wq_pack_int4([1, -2]).tolist() == [225]
+    assert wq.wq_pack_int4([7, -8]).tolist() == [135]
+    assert wq.wq_pack_int4([3, -1, 5]).tolist() == [0xF3, 0x05]
+    data = np.arange(256, dtype=np.uint8)
+    codes = wq.wq_unpack_int4(data, 512)
+    assert np.array_equal(wq.wq_pack_int4(codes), data)
+    assert wq.wq_packed_size(7_000_000_000, 4) == 3_500_000_000
+    assert wq.wq_packed_size(7_000_000_000, 16) == 14_000_000_000
+    assert wq.wq_packed_size(3, 4) == 2
+    assert wq.wq_packed_size(-1, 4) == -1
+    for bad in ([8], [-9]):
+        with pytest.raises(ValueError, match="WQ_ERR_RANGE"):
+            wq.wq_pack_int4(bad)
+
+
+def test_pack_helpers_agree_with_oracle(wq, orc):
+    codes = np.random.default_rng(0).integers(-8, 8, 1001).astype(np.int32)
+    assert np.array_equal(wq.wq_pack_int4(codes), orc.pack_int4(codes))
+    packed = orc.pack_int4(codes)
+    assert np.array_equal(wq.wq_unpack_int4(packed, 1001), orc.unpack_int4(packed, 1001))
+
+
+def test_status_strings(wq):
+    L = wq.lib()
+    assert L.wq_status_string(0) == b"WQ_OK"
+    assert L.wq_status_string(-5) == b"WQ_ERR_WORKSPACE"
+    assert L.wq_status_string(99) == b"WQ_ERR_UNKNOWN"
+
+
+def _weight(wq, **kw):
+    base = dict(format=3, group=64, experts=1, n=64, k=256, codes=0x1000, scales=None,
+                zeros=None, qscale=0x2000, super_scale=0x3000, code_scale=0x4000,
+                code_zero=0x5000, zp=32)
+    base.update(kw)
+    return wq._CWeight(*[base[f] for f, _ in wq._CWeight._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=100), -2),                 # k not a multiple of 64
+    (dict(format=9), -2),              # unknown format
+    (dict(group=32), -2),              # CCQ needs group 64
+    (dict(codes=None), -1),            # null codes
+    (dict(codes=0x1001), -3),          # misaligned
+    (dict(qscale=None), -1),
+    (dict(zp=200), -2),
+    (dict(zp=33), -2),                 # products need a power-of-two CCQ zero point
+    (dict(n=0), -1),
+    (dict(format=1, group=128, scales=0x6000), -2),
+    (dict(format=2, scales=0x6000, zeros=None), -1),
+])
+def test_gemm_rejects_bad_descriptors_without_launch(wq, kw, status):
+    L = wq.lib()
+    w = _weight(wq, **kw)
+    st = L.wq_gemm(ctypes.c_void_p(0x7000), 4, ctypes.byref(w), ctypes.c_void_p(0x8000), None)
+    assert st == status, L.wq_last_error()
+    assert L.wq_last_error()
+
+
+def test_gemm_argument_checks(wq):
+    L = wq.lib()
+    w = _weight(wq)
+    assert L.wq_gemm(ctypes.c_void_p(0x7000), -1, ctypes.byref(w), ctypes.c_void_p(0x8000), None) == -1
+    assert L.wq_gemm(None, 0, ctypes.byref(w), None, None) == 0  # m == 0 is a no-op
+    assert L.wq_gemm(None, 2, ctypes.byref(w), ctypes.c_void_p(0x8000), None) == -1
+    assert L.wq_gemm(ctypes.c_void_p(0x7008), 2, ctypes.byref(w), ctypes.c_void_p(0x8000), None) == -3
+    w2 = _weight(wq, experts=3)
+    assert L.wq_gemm(ctypes.c_void_p(0x7000), 2, ctypes.byref(w2), ctypes.c_void_p(0x8000), None) == -1
+    assert L.wq_dequantize(ctypes.byref(w), None, None) == -1
+
+
+def test_moe_argument_checks(wq):
+    L = wq.lib()
+    E, H, I, T, K = 4, 256, 128, 8, 2
+    g = _weight(wq, experts=E, n=I, k=H)
+    u = _weight(wq, experts=E, n=I, k=H)
+    d = _weight(wq, experts=E, n=H, k=I)
+    need = L.wq_moe_workspace_bytes(T, K, E, H, I)
+    assert need >= T * K * (I * 2 + H * 4)
+    x, ids, wts, y, ws = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
+    call = lambda gg, uu, dd, wsb, hidden=H: L.wq_moe_ffn(x, T, hidden, ids, wts, K, ctypes.byref(gg),
+                                                          ctypes.byref(uu), ctypes.byref(dd), y, ws,
+                                                          wsb, None)
+    assert call(g, u, d, need - 1) == -5          # workspace too small
+    bad_d = _weight(wq, experts=E, n=H, k=256)    # down's k must equal inter
+    assert call(g, u, bad_d, need) == -1
+    bad_u = _weight(wq, experts=E + 1, n=I, k=H)
+    assert call(g, bad_u, d, need) == -1
+    mixed = _weight(wq, experts=E, n=I, k=H, format=1, scales=0x6000, qscale=None)
+    assert call(g, mixed, d, need) == -2          # gate and up must share a format
+    big = _weight(wq, experts=1000, n=I, k=H)
+    assert call(big, big, _weight(wq, experts=1000, n=H, k=I), need) == -2
+    assert L.wq_moe_route(ids, T, K, 0, ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000), None, 0, None) == -1

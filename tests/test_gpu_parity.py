@@ -1,0 +1,223 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle, on seeded inputs.
+
+Sizes here are ones the oracle finishes in seconds but that span several tiles, K chunks and
+ragged tails.  Decode is compared bit for bit; products within the tolerance of
+tests/wq_testutil.py.  Inputs come from synth (weights, activations, routing) and the
+oracle's quantizers (packed bytes) -- never from the HIP path.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from wq_testutil import assert_close, to_device, torch_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {"int4": oracle.INT4, "affine2": oracle.AFFINE2, "ccq": oracle.CCQ}
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import torch
+
+    import weight_only_bit_amd as wq
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wq.lib()
+    return wq
+
+
+def _quant(fmt, shape, seed, group=64):
+    w = synth.weights_f32(shape, *seed)
+    return oracle.quantize(w, fmt, group=group)
+
+
+def _random_packed(fmt, E, n, k, seed, group=64):
+    arr = synth.random_packed(fmt, E, n, k, *seed, group=group)
+    return oracle.Packed(fmt, n, k, E, group, arr.get("codes"), arr.get("scales"), arr.get("zeros"),
+                         arr.get("qscale"), arr.get("super_scale"), arr.get("code_scale"),
+                         arr.get("code_zero"), 32)
+
+
+# ---------------------------------------------------------------------------------------------
+# Dequantize: bit-exact
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+@pytest.mark.parametrize("src", ["quantized", "random"])
+def test_dequantize_bit_exact(wq, name, src):
+    fmt = FMTS["int4" if name == "int4pc" else name]
+    group = 0 if name == "int4pc" else 64
+    E, n, k = 2, 40, 320  # 5 groups: an odd count exercises the half-used qscale byte
+    _say(f"dequant {name} {src} E={E} n={n} k={k}")
+    if src == "quantized":
+        p = _quant(fmt, (E, n, k), (1, fmt, group), group=group)
+    else:
+        p = _random_packed(fmt, E, n, k, (2, fmt, group), group=group)
+    got = torch_bf16_bits(wq.wq_dequantize(to_device(p)))
+    for e in range(E):
+        ref = oracle.dequantize(p, e)
+        assert np.array_equal(got[e], ref), f"expert {e}: {(got[e] != ref).sum()} mismatches"
+
+
+def test_dequantize_ccq_every_code(wq):
+    # rows r with code scale 1 and code zero 256 r: the 128 rows cover all 2^15 codes, every
+    # group scale 0..15, and a non-trivial super scale per row
+    rows, k = 128, 1024
+    g = np.random.default_rng(21)
+    codes = np.tile(np.arange(256, dtype=np.uint8), (rows, 1))[None]
+    sq = g.integers(0, 16, (rows, k // 64), dtype=np.uint8)
+    qscale = (sq[:, 0::2] | (sq[:, 1::2] << 4)).astype(np.uint8)[None]
+    p = oracle.Packed(oracle.CCQ, rows, k, 1, 64, codes, qscale=qscale,
+                      super_scale=g.uniform(1e-4, 1e-3, (1, rows)).astype(np.float32),
+                      code_scale=np.ones((1, rows), np.float32),
+                      code_zero=(256.0 * np.arange(rows, dtype=np.float32))[None], zp=32)
+    got = torch_bf16_bits(wq.wq_dequantize(to_device(p)))[0]
+    assert np.array_equal(got, oracle.dequantize(p))
+
+
+def test_dequantize_ccq_rounding_and_clamp_edges(wq):
+    # code scales / zeros that put fma results on .5 ties, below 0 and above 2^15 - 1
+    rows, k = 16, 256
+    g = np.random.default_rng(22)
+    cs = np.array([0.5, 1.5, 128.5, 127.25, 200.0, 300.0, 1.0, 64.0625,
+                   0.75, 2.5, 128.0, 129.0, 1e-3, 255.0, 128.49, 97.7], np.float32)
+    cz = np.array([0.5, -0.5, -100.0, 0.25, 0.0, -5.0, 32760.0, 10.5,
+                   -0.49, 0.5, 32767.0, -129.0, 0.5, 0.0, 1.5, 3.0], np.float32)
+    codes = g.integers(0, 256, (1, rows, k // 4), dtype=np.uint8)
+    codes[0, :, :256 // 4] = np.arange(64, dtype=np.uint8)[None] * 4 + 3
+    sq = g.integers(1, 16, (rows, k // 128), dtype=np.uint8)
+    p = oracle.Packed(oracle.CCQ, rows, k, 1, 64, codes, qscale=(sq | (sq << 4))[None],
+                      super_scale=np.full((1, rows), 3e-4, np.float32), code_scale=cs[None],
+                      code_zero=cz[None], zp=32)
+    got = torch_bf16_bits(wq.wq_dequantize(to_device(p)))[0]
+    assert np.array_equal(got, oracle.dequantize(p))
+
+
+# ---------------------------------------------------------------------------------------------
+# Dense product
+# ---------------------------------------------------------------------------------------------
+
+DENSE_SHAPES = [(80, 576), (128, 1024), (512, 512)]
+
+
+@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+@pytest.mark.parametrize("nk", DENSE_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("m", [1, 3, 16, 17, 32, 33, 70])
+def test_gemm_parity(wq, name, nk, m):
+    import torch
+
+    fmt = FMTS["int4" if name == "int4pc" else name]
+    group = 0 if name == "int4pc" else 64
+    n, k = nk
+    _say(f"gemm {name} n={n} k={k} m={m}")
+    p = _quant(fmt, (n, k), (3, fmt, group, n, k), group=group)
+    x = synth.acts_bf16((m, k), 4, m, k)
+    ref = oracle.gemm(x, p)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    y = wq.wq_gemm(xd, to_device(p))
+    assert_close(torch_bf16_bits(y), ref, f"gemm {name} {n}x{k} m={m}")
+
+
+def test_gemm_deterministic(wq):
+    import torch
+
+    p = _quant(oracle.CCQ, (256, 2048), (5,))
+    x = torch.from_numpy(synth.acts_bf16((8, 2048), 6).view(np.int16)).cuda()
+    d = to_device(p)
+    a = torch_bf16_bits(wq.wq_gemm(x, d))
+    b = torch_bf16_bits(wq.wq_gemm(x, d))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+def test_gemm_decodes_every_weight_bit_exact(wq, name):
+    # Identity activations: row m of x = e_(c0+m) makes y[m][n] = W_hat[n][c0+m], one exact
+    # product rounded back to the same bf16 -- so the product path's decode of every weight
+    # must equal the oracle's decoded bits.
+    import torch
+
+    fmt = FMTS["int4" if name == "int4pc" else name]
+    group = 0 if name == "int4pc" else 64
+    n, k = 48, 320
+    p = _quant(fmt, (n, k), (7, fmt, group), group=group)
+    ref = oracle.dequantize(p)
+    d = to_device(p)
+    for c0 in range(0, k, 32):
+        x = np.zeros((32, k), np.uint16)
+        x[np.arange(32), c0 + np.arange(32)] = 0x3F80
+        y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
+        assert np.array_equal(y.T, ref[:, c0:c0 + 32]), f"columns {c0}..{c0 + 31}"
+
+
+# ---------------------------------------------------------------------------------------------
+# MoE routing and expert FFN
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t,topk,experts,kind", [(1, 8, 64, "uniform"), (7, 2, 8, "uniform"),
+                                                 (300, 8, 64, "uniform"), (4096, 8, 64, "zipf"),
+                                                 (33, 4, 300, "uniform")])
+def test_route_exact(wq, t, topk, experts, kind):
+    import torch
+
+    _say(f"route t={t} topk={topk} E={experts} {kind}")
+    gen = synth.routing_zipf if kind == "zipf" else synth.routing_uniform
+    ids, _ = gen(t, topk, experts, 8, t)
+    off_ref, pairs_ref = oracle.moe_route(ids, experts)
+    off, pairs = wq.wq_moe_route(torch.from_numpy(ids).cuda(), experts)
+    assert np.array_equal(off.cpu().numpy(), off_ref)
+    assert np.array_equal(pairs.cpu().numpy(), pairs_ref)
+
+
+MOE_CASES = [
+    # name, E, hidden, inter, tokens, topk
+    ("ccq", 8, 256, 192, 5, 2),
+    ("ccq", 8, 512, 320, 40, 4),
+    ("int4pc", 6, 256, 128, 12, 3),
+    ("affine2", 4, 256, 192, 9, 2),
+    ("int4", 4, 192, 128, 70, 2),
+]
+
+
+@pytest.mark.parametrize("case", MOE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_moe_ffn_parity(wq, case):
+    import torch
+
+    name, E, H, I, T, topk = case
+    fmt = FMTS["int4" if name == "int4pc" else name]
+    group = 0 if name == "int4pc" else 64
+    _say(f"moe {case}")
+    gate = _quant(fmt, (E, I, H), (9, 1, E, H, I), group=group)
+    up = _quant(fmt, (E, I, H), (9, 2, E, H, I), group=group)
+    down = _quant(fmt, (E, H, I), (9, 3, E, H, I), group=group)
+    x = synth.acts_bf16((T, H), 10, T, H)
+    ids, wts = synth.routing_uniform(T, topk, E, 11, T)
+    ref = oracle.moe_ffn(x, ids, wts, gate, up, down)
+    y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(wts).cuda(), to_device(gate), to_device(up), to_device(down))
+    assert_close(torch_bf16_bits(y), ref, f"moe {case}")
+
+
+def test_moe_all_tokens_one_expert(wq):
+    # every token routed to experts 0 and 1: a 40-row expert exercises two row super-tiles
+    import torch
+
+    E, H, I, T = 4, 256, 128, 40
+    gate = _quant(oracle.CCQ, (E, I, H), (12, 1))
+    up = _quant(oracle.CCQ, (E, I, H), (12, 2))
+    down = _quant(oracle.CCQ, (E, H, I), (12, 3))
+    x = synth.acts_bf16((T, H), 13)
+    ids = np.tile(np.array([[1, 0]], np.int32), (T, 1))
+    wts = np.tile(np.array([[0.75, 0.25]], np.float32), (T, 1))
+    ref = oracle.moe_ffn(x, ids, wts, gate, up, down)
+    y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(wts).cuda(), to_device(gate), to_device(up), to_device(down))
+    assert_close(torch_bf16_bits(y), ref, "moe one expert")

@@ -1,0 +1,299 @@
+// wq_api.hip -- the C ABI of libwq.so (declared in include/wq.h): host-side validation,
+// kernel selection and launches.  No compute happens on the host; nothing here allocates
+// device memory or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/wq.h"
+#include "wq_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+wq_status fail(wq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+wq_status fail(wq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+wq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return WQ_OK;
+  return fail(WQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The product kernels decode CCQ weights as fma(u, s, -zp*s), exact when zp*s is exact: zp
+// must then be zero or a power of two (the format's zero point is 32).
+wq_status check_product_zp(const wq_weight* w, const char* what) {
+  if (w->format == WQ_FMT_CCQ2 && (w->zp & (w->zp - 1)) != 0)
+    return fail(WQ_ERR_UNSUPPORTED, "%s: products need a CCQ zero point of 0 or a power of two", what);
+  return WQ_OK;
+}
+
+// Validate a packed-weight descriptor; `what` names it in error messages.
+wq_status check_weight(const wq_weight* w, const char* what) {
+  if (!w) return fail(WQ_ERR_ARG, "%s: null descriptor", what);
+  if (w->n <= 0 || w->k <= 0 || w->experts <= 0)
+    return fail(WQ_ERR_ARG, "%s: n, k and experts must be positive", what);
+  if (w->k % 64 != 0) return fail(WQ_ERR_UNSUPPORTED, "%s: k = %lld is not a multiple of 64", what, (long long)w->k);
+  if (w->n > (1ll << 31) || w->k > (1ll << 31))
+    return fail(WQ_ERR_UNSUPPORTED, "%s: n and k must be below 2^31", what);
+  if (!w->codes) return fail(WQ_ERR_ARG, "%s: null codes", what);
+  if (!aligned16(w->codes)) return fail(WQ_ERR_ALIGN, "%s: codes not 16-byte aligned", what);
+  switch (w->format) {
+    case WQ_FMT_INT4:
+      if (w->group != 64 && w->group != 0)
+        return fail(WQ_ERR_UNSUPPORTED, "%s: INT4 group must be 64 or 0 (per channel)", what);
+      if (!w->scales) return fail(WQ_ERR_ARG, "%s: null scales", what);
+      if (!aligned16(w->scales)) return fail(WQ_ERR_ALIGN, "%s: scales not 16-byte aligned", what);
+      break;
+    case WQ_FMT_INT2_AFFINE:
+      if (w->group != 64) return fail(WQ_ERR_UNSUPPORTED, "%s: affine 2-bit needs group 64", what);
+      if (!w->scales || !w->zeros) return fail(WQ_ERR_ARG, "%s: null scales or zeros", what);
+      if (!aligned16(w->scales) || !aligned16(w->zeros))
+        return fail(WQ_ERR_ALIGN, "%s: scales/zeros not 16-byte aligned", what);
+      break;
+    case WQ_FMT_CCQ2:
+      if (w->group != 64) return fail(WQ_ERR_UNSUPPORTED, "%s: CCQ needs group 64", what);
+      if (!w->qscale || !w->super_scale || !w->code_scale || !w->code_zero)
+        return fail(WQ_ERR_ARG, "%s: null CCQ scale arrays", what);
+      if (!aligned16(w->qscale) || !aligned16(w->super_scale) || !aligned16(w->code_scale) ||
+          !aligned16(w->code_zero))
+        return fail(WQ_ERR_ALIGN, "%s: CCQ scale arrays not 16-byte aligned", what);
+      if (w->zp < 0 || w->zp > 127)
+        return fail(WQ_ERR_UNSUPPORTED, "%s: CCQ zero point must lie in 0..127", what);
+      break;
+    default:
+      return fail(WQ_ERR_UNSUPPORTED, "%s: unknown format %d", what, w->format);
+  }
+  return WQ_OK;
+}
+
+wq::DevWeight dev_weight(const wq_weight* w) {
+  wq::DevWeight d;
+  d.codes = w->codes;
+  d.scales = w->scales;
+  d.zeros = w->zeros;
+  d.qscale = w->qscale;
+  d.super_scale = w->super_scale;
+  d.code_scale = w->code_scale;
+  d.code_zero = w->code_zero;
+  d.n = w->n;
+  d.k = w->k;
+  d.group = w->group;
+  d.zp = w->zp;
+  return d;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct MoeWs {
+  int32_t* offsets;
+  int32_t* sorted;
+  uint16_t* h;
+  float* d;
+  size_t bytes;
+};
+
+MoeWs moe_layout(void* ws, int64_t t, int32_t topk, int32_t experts, int64_t hidden, int64_t inter) {
+  MoeWs L;
+  const size_t pairs = (size_t)t * (size_t)topk;
+  size_t off = 0;
+  char* b = static_cast<char*>(ws);
+  L.offsets = reinterpret_cast<int32_t*>(b + off);
+  off = align_up(off + sizeof(int32_t) * ((size_t)experts + 1));
+  L.sorted = reinterpret_cast<int32_t*>(b + off);
+  off = align_up(off + sizeof(int32_t) * pairs);
+  L.h = reinterpret_cast<uint16_t*>(b + off);
+  off = align_up(off + sizeof(uint16_t) * pairs * (size_t)inter);
+  L.d = reinterpret_cast<float*>(b + off);
+  off = align_up(off + sizeof(float) * pairs * (size_t)hidden);
+  L.bytes = off;
+  return L;
+}
+
+constexpr int32_t kMaxExperts = 512;
+
+}  // namespace
+
+extern "C" {
+
+const char* wq_status_string(int32_t st) {
+  switch (st) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_ERR_ARG: return "WQ_ERR_ARG";
+    case WQ_ERR_UNSUPPORTED: return "WQ_ERR_UNSUPPORTED";
+    case WQ_ERR_ALIGN: return "WQ_ERR_ALIGN";
+    case WQ_ERR_RANGE: return "WQ_ERR_RANGE";
+    case WQ_ERR_WORKSPACE: return "WQ_ERR_WORKSPACE";
+    case WQ_ERR_HIP: return "WQ_ERR_HIP";
+    default: return "WQ_ERR_UNKNOWN";
+  }
+}
+
+const char* wq_last_error(void) { return g_last_error.c_str(); }
+
+wq_status wq_pack_int4(const int32_t* codes, int64_t n, uint8_t* out) {
+  if (n < 0 || (n > 0 && (!codes || !out))) return fail(WQ_ERR_ARG, "wq_pack_int4: bad arguments");
+  for (int64_t i = 0; i < n; ++i)
+    if (codes[i] < -8 || codes[i] > 7)
+      return fail(WQ_ERR_RANGE, "wq_pack_int4: code %d at index %lld outside -8..7", codes[i], (long long)i);
+  for (int64_t b = 0; b < (n + 1) / 2; ++b) {
+    const int32_t first = codes[2 * b];
+    const int32_t second = (2 * b + 1 < n) ? codes[2 * b + 1] : 0;
+    out[b] = (uint8_t)((first & 0xF) | ((second & 0xF) << 4));
+  }
+  return WQ_OK;
+}
+
+wq_status wq_unpack_int4(const uint8_t* data, int64_t n, int32_t* out) {
+  if (n < 0 || (n > 0 && (!data || !out))) return fail(WQ_ERR_ARG, "wq_unpack_int4: bad arguments");
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t v = (data[i >> 1] >> (4 * (i & 1))) & 0xF;
+    out[i] = (v ^ 8) - 8;
+  }
+  return WQ_OK;
+}
+
+int64_t wq_packed_size(int64_t n_codes, int32_t bits) {
+  if (n_codes < 0 || bits < 1 || bits > 32) return -1;
+  return (n_codes * (int64_t)bits + 7) / 8;
+}
+
+wq_status wq_dequantize(const wq_weight* w, uint16_t* out, void* stream) {
+  wq_status st = check_weight(w, "wq_dequantize");
+  if (st != WQ_OK) return st;
+  if (!out) return fail(WQ_ERR_ARG, "wq_dequantize: null output");
+  if (!aligned16(out)) return fail(WQ_ERR_ALIGN, "wq_dequantize: output not 16-byte aligned");
+  return hip_status(wq::launch_dequant(w->format, dev_weight(w), w->experts, out,
+                                       static_cast<hipStream_t>(stream)),
+                    "wq_dequantize launch");
+}
+
+wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y, void* stream) {
+  wq_status st = check_weight(w, "wq_gemm");
+  if (st != WQ_OK) return st;
+  if ((st = check_product_zp(w, "wq_gemm")) != WQ_OK) return st;
+  if (m < 0) return fail(WQ_ERR_ARG, "wq_gemm: negative m");
+  if (w->experts != 1) return fail(WQ_ERR_ARG, "wq_gemm: a dense weight has experts == 1");
+  if (m == 0) return WQ_OK;
+  if (!x || !y) return fail(WQ_ERR_ARG, "wq_gemm: null x or y");
+  if (!aligned16(x) || !aligned16(y)) return fail(WQ_ERR_ALIGN, "wq_gemm: x or y not 16-byte aligned");
+  if (m > (1ll << 31)) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: m must be below 2^31");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  wq::SkinnyArgs a{};
+  a.w0 = dev_weight(w);
+  a.w1 = a.w0;
+  a.a = x;
+  a.a_stride = w->k;
+  a.out = y;
+  a.out_stride = w->n;
+  a.M = m;
+  a.N = w->n;
+  a.K = w->k;
+  const int mt = (m <= 16) ? 1 : 2;
+  const int64_t rows = 16 * mt;
+  const int64_t n_tiles = (w->n + 15) / 16;
+  // Split K across the 4 waves when 4-tile workgroups would leave the 256 CUs idle.
+  const int ksplit = (n_tiles / 4 < 512 && w->k % 256 == 0) ? 4 : 1;
+  return hip_status(wq::launch_skinny(w->format, wq::MODE_DENSE, mt, ksplit, a, 1,
+                                      (m + rows - 1) / rows, s),
+                    "wq_gemm launch");
+}
+
+size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t hidden,
+                              int64_t inter) {
+  if (t < 0 || topk <= 0 || experts <= 0 || hidden <= 0 || inter <= 0) return 0;
+  return moe_layout(nullptr, t, topk, experts, hidden, inter).bytes;
+}
+
+wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t experts,
+                       int32_t* expert_offsets, int32_t* sorted_pairs, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (t < 0 || topk <= 0 || experts <= 0) return fail(WQ_ERR_ARG, "wq_moe_route: bad sizes");
+  if (experts > kMaxExperts) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_route: at most %d experts", kMaxExperts);
+  if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_route: too many pairs");
+  if (!expert_offsets || (t > 0 && (!topk_ids || !sorted_pairs)))
+    return fail(WQ_ERR_ARG, "wq_moe_route: null pointer");
+  return hip_status(wq::launch_route(topk_ids, t * topk, experts, expert_offsets, sorted_pairs,
+                                     static_cast<hipStream_t>(stream)),
+                    "wq_moe_route launch");
+}
+
+wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
+                     const float* topk_weights, int32_t topk, const wq_weight* gate,
+                     const wq_weight* up, const wq_weight* down, uint16_t* y, void* ws,
+                     size_t ws_bytes, void* stream) {
+  wq_status st;
+  if ((st = check_weight(gate, "wq_moe_ffn gate")) != WQ_OK) return st;
+  if ((st = check_weight(up, "wq_moe_ffn up")) != WQ_OK) return st;
+  if ((st = check_weight(down, "wq_moe_ffn down")) != WQ_OK) return st;
+  if ((st = check_product_zp(gate, "wq_moe_ffn gate")) != WQ_OK) return st;
+  if ((st = check_product_zp(down, "wq_moe_ffn down")) != WQ_OK) return st;
+  if (t < 0 || topk <= 0 || hidden <= 0) return fail(WQ_ERR_ARG, "wq_moe_ffn: bad sizes");
+  const int64_t E = gate->experts, I = gate->n;
+  if (up->experts != E || down->experts != E)
+    return fail(WQ_ERR_ARG, "wq_moe_ffn: gate, up and down must have the same expert count");
+  if (E > kMaxExperts) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: at most %d experts", kMaxExperts);
+  if (gate->k != hidden || up->k != hidden || up->n != I || down->n != hidden || down->k != I)
+    return fail(WQ_ERR_ARG, "wq_moe_ffn: shapes must be gate/up [E][inter][hidden], down [E][hidden][inter]");
+  if (gate->format != up->format || gate->group != up->group || gate->zp != up->zp)
+    return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: gate and up must share format, group and zp");
+  if (hidden % 4 != 0) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: hidden must be a multiple of 4");
+  if (t == 0) return WQ_OK;
+  if (!x || !topk_ids || !topk_weights || !y || !ws) return fail(WQ_ERR_ARG, "wq_moe_ffn: null pointer");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws))
+    return fail(WQ_ERR_ALIGN, "wq_moe_ffn: x, y and ws must be 16-byte aligned");
+  if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: too many pairs");
+  MoeWs L = moe_layout(ws, t, topk, (int32_t)E, hidden, I);
+  if (ws_bytes < L.bytes)
+    return fail(WQ_ERR_WORKSPACE, "wq_moe_ffn: workspace %zu < %zu bytes", ws_bytes, L.bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = wq::launch_route(topk_ids, t * topk, (int32_t)E, L.offsets, L.sorted, s);
+  if (e != hipSuccess) return hip_status(e, "wq_moe_ffn route");
+
+  wq::SkinnyArgs a{};
+  a.offsets = L.offsets;
+  a.sorted_pairs = L.sorted;
+  a.topk = topk;
+  // gate + up -> h (bf16, rows in expert-sorted order)
+  a.w0 = dev_weight(gate);
+  a.w1 = dev_weight(up);
+  a.a = x;
+  a.a_stride = hidden;
+  a.out = L.h;
+  a.out_stride = I;
+  a.N = I;
+  a.K = hidden;
+  const int mt = ((double)t * topk / (double)E <= 8.0) ? 1 : 2;
+  e = wq::launch_skinny(gate->format, wq::MODE_GATEUP, mt, 1, a, E, 1, s);
+  if (e != hipSuccess) return hip_status(e, "wq_moe_ffn gate/up");
+  // down -> d (f32, rows indexed by pair id)
+  a.w0 = dev_weight(down);
+  a.w1 = a.w0;
+  a.a = L.h;
+  a.a_stride = I;
+  a.out = L.d;
+  a.out_stride = hidden;
+  a.N = hidden;
+  a.K = I;
+  e = wq::launch_skinny(down->format, wq::MODE_DOWN, mt, 1, a, E, 1, s);
+  if (e != hipSuccess) return hip_status(e, "wq_moe_ffn down");
+  e = wq::launch_combine(L.d, topk_weights, t, topk, hidden, y, s);
+  return hip_status(e, "wq_moe_ffn combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// wq_kernels.hpp -- kernel argument structs and launcher declarations shared by the HIP
+// translation units of libwq.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wq_device.hpp"
+
+namespace wq {
+
+// Arguments of the decode-streaming ("skinny") MFMA kernels.
+struct SkinnyArgs {
+  DevWeight w0;                 // dense W / MoE gate / MoE down
+  DevWeight w1;                 // MoE up (gate+up mode only)
+  const uint16_t* a;            // activations: dense x [M][K]; MoE x [T][K]; MoE h [P][K]
+  int64_t a_stride;             // elements per activation row
+  void* out;                    // dense y bf16 [M][N]; MoE h bf16 [P][N]; MoE d f32 [P][N]
+  int64_t out_stride;           // elements per output row
+  int64_t M;                    // dense rows
+  int64_t N, K;
+  const int32_t* offsets;       // MoE: expert_offsets [E+1]
+  const int32_t* sorted_pairs;  // MoE: pair ids grouped by expert
+  int32_t topk;
+};
+
+enum { MODE_DENSE = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
+
+// Launch the skinny kernel for format `fmt`; m_tiles = 1 or 2 (16 or 32 activation rows per
+// pass); ksplit = 1 or 4 (waves of a workgroup split K); grid_y = experts (MoE) or 1;
+// grid_z = row super-tiles (dense).
+hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
+                         int64_t grid_y, int64_t grid_z, hipStream_t stream);
+
+hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t* out,
+                          hipStream_t stream);
+
+hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int32_t* offsets,
+                        int32_t* sorted_pairs, hipStream_t stream);
+
+hipError_t launch_combine(const float* d, const float* weights, int64_t t, int32_t topk,
+                          int64_t hidden, uint16_t* y, hipStream_t stream);
+
+// Arguments of the LDS-staged MFMA GEMM (large row counts).
+struct TiledArgs {
+  DevWeight w0, w1;             // as SkinnyArgs
+  const uint16_t* a;
+  int64_t a_stride;
+  void* out;
+  int64_t out_stride;
+  int64_t M, N, K;
+  const int32_t* offsets;
+  const int32_t* sorted_pairs;
+  int32_t topk;
+  int32_t experts;
+  const int32_t* tile_expert;   // MoE: per m-tile work item, its expert (device)
+  const int32_t* tile_row;      // MoE: per m-tile work item, its first row within the expert
+  const int32_t* tile_count;    // MoE: number of m-tile work items (device scalar)
+};
+
+hipError_t launch_tiled(int fmt, int mode, const TiledArgs& args, int64_t max_mtiles,
+                        hipStream_t stream);
+
+hipError_t launch_tile_list(const int32_t* offsets, int32_t experts, int32_t bm,
+                            int32_t* tile_expert, int32_t* tile_row, int32_t* tile_count,
+                            hipStream_t stream);
+
+}  // namespace wq
