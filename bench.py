@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-only low-bit decode path on one MI355X.
+
+Default workload (one step): a mixed-precision MoE stack decode step at batch 32 -- 54 MoE
+layers, each 64 experts with hidden 8192 and expert intermediate 3584, top-8 routing; layers
+0-6 hold INT4 per-channel weights and layers 7-53 CCQ (6,4,3) group-64 weights (the w4w2 layer
+map of the FastDeploy WINT2 deployment).  All 88.6 GB of packed weights are resident in HBM;
+every layer reads the same bf16 activations and writes its own output.  One step runs, per
+layer: routing, expert gate+up (fused SiLU*up), expert down and the weighted combine.
+
+Reported: weight-stream GB/s (packed bytes of the experts a step routes to / step time),
+tokens/s, the roofline of the dominant kernel (CCQ gate+up) from HIP events around each of
+its launches in the timed region, and the CPU oracle timed on a bounded sample.
+
+Inputs are synthetic: packed codes and scales are seeded random draws with the layout and
+magnitudes of quantized N(0, 0.02) weights (the kernels' cost does not depend on code values);
+activations N(0, 1); uniform top-8 routing with softmax weights.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=54, help="MoE layers in the stack")
+    ap.add_argument("--int4-layers", type=int, default=7, help="leading INT4 per-channel layers")
+    ap.add_argument("--tokens", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens per sampled layer for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def make_layer(wq, synth, fmt, E, H, I, seed, group):
+    """gate, up, down PackedWeight for one layer, drawn on the GPU."""
+    ws = []
+    for j, (n, k) in enumerate(((I, H), (I, H), (H, I))):
+        arr = synth.random_packed_device(fmt, E, n, k, seed * 16 + j, group=group)
+        ws.append(wq.PackedWeight(fmt, n, k, E, group, *(arr.get(f) for f in (
+            "codes", "scales", "zeros", "qscale", "super_scale", "code_scale", "code_zero")), 32))
+    return ws
+
+
+def to_host_packed(oracle, w):
+    """Device PackedWeight -> oracle.Packed (host copies of the same bytes)."""
+    import numpy as np
+
+    def h(t):
+        if t is None:
+            return None
+        a = t.cpu().numpy()
+        return a.view(np.uint16) if a.dtype == np.int16 else a
+
+    return oracle.Packed(w.format, w.n, w.k, w.experts, w.group, h(w.codes), h(w.scales),
+                         h(w.zeros), h(w.qscale), h(w.super_scale), h(w.code_scale),
+                         h(w.code_zero), w.zp)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the decode path keeps every expert of a layer on "
+              f"one device (no sharding, no collectives); got --gpus {args.gpus}, WORLD_SIZE {world}.",
+              flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_only_bit_amd as wq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wq.lib()
+    dev = torch.device("cuda:0")
+    E, H, I, K = 64, 8192, 3584, 8
+    T = args.tokens
+    L = args.layers
+    n4 = min(args.int4_layers, L)
+
+    # ---------------- resident stack ----------------
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        fmt, group = (wq.FMT_INT4, 0) if l < n4 else (wq.FMT_CCQ2, 64)
+        layers.append(make_layer(wq, synth, fmt, E, H, I, 1000 + l, group))
+        if l % 8 == 7 or l == L - 1:
+            torch.cuda.synchronize()
+            log(f"generated layers 0..{l} ({time.time() - t0:.1f} s)")
+    resident = sum(w.nbytes() for lay in layers for w in lay)
+    x = torch.from_numpy(synth.acts_bf16((T, H), 500).view(np.int16)).to(dev)
+    routes = []
+    for l in range(L):
+        ids, wts = synth.routing_uniform(T, K, E, 600, l)
+        routes.append((ids, wts, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)))
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(T * K, dtype=torch.int32, device=dev)
+    h = torch.empty((T * K, I), dtype=torch.bfloat16, device=dev)
+    d = torch.empty((T * K, H), dtype=torch.float32, device=dev)
+    ys = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+
+    # Algorithmic bytes: packed weights of the experts each layer routes to.
+    per_expert = [[w.nbytes() // E for w in lay] for lay in layers]
+    touched = [len(np.unique(r[0])) for r in routes]
+    step_weight_bytes = sum(touched[l] * sum(per_expert[l]) for l in range(L))
+    step_act_bytes = L * 2 * T * H * 2  # x read + y written per layer
+    ccq_layers = [l for l in range(L) if l >= n4]
+
+    L_ = wq.lib()
+
+    def layer(l, ev=None):
+        g, u, dn = layers[l]
+        ids_d, wts_d = routes[l][2], routes[l][3]
+        st = torch.cuda.current_stream()
+        wq._check(L_.wq_moe_route(wq._ptr(ids_d), T, K, E, wq._ptr(offsets), wq._ptr(pairs), None, 0,
+                                  wq._stream()), "route")
+        if ev is not None:
+            ev[0].record(st)
+        wq.wq_moe_gate_up(x, offsets, pairs, K, g, u, h=h)
+        if ev is not None:
+            ev[1].record(st)
+        wq.wq_moe_down(h, T, K, offsets, pairs, dn, d=d)
+        wq.wq_moe_combine(d, wts_d, y=ys[l])
+
+    def step(evs=None):
+        for l in range(L):
+            layer(l, evs.get(l) if evs is not None else None)
+
+    # ---------------- warmup + timed steps ----------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs_all = [{l: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for l in ccq_layers} for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(evs_all[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    gu_ms = [evs[l][0].elapsed_time(evs[l][1]) for evs in evs_all for l in ccq_layers]
+    gu_avg_ms = float(np.mean(gu_ms)) if gu_ms else float("nan")
+    # bytes of one CCQ gate+up launch: gate and up of the touched experts + x read + h written
+    gu_bytes = float(np.mean([touched[l] * (per_expert[l][0] + per_expert[l][1]) for l in ccq_layers])) \
+        + T * H * 2 + T * K * I * 2
+    gu_gbs = gu_bytes / (gu_avg_ms * 1e-3) / 1e9
+
+    value = step_weight_bytes / (ms_step * 1e-3) / 1e9
+    tok_s = T / (ms_step * 1e-3)
+    log(f"step {ms_step:.3f} ms, weight stream {value:.1f} GB/s, {tok_s:.1f} tok/s; "
+        f"CCQ gate+up {gu_avg_ms * 1e3:.1f} us avg -> {gu_gbs:.1f} GB/s")
+
+    # ---------------- CPU baseline (oracle on a bounded sample) + spot parity ----------------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from wq_testutil import assert_close, torch_bf16_bits
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        sample_layers = [n4] + ([0] if n4 > 0 else [])
+        tot_bytes, tot_s, errs = 0, 0.0, []
+        for l in sample_layers:
+            g, u, dn = (to_host_packed(oracle, w) for w in layers[l])
+            ids, wts = routes[l][0], routes[l][1]
+            toks = np.arange(min(args.cpu_tokens, T), dtype=np.int32)
+            xh = x.cpu().numpy().view(np.uint16)
+            t1 = time.perf_counter()
+            yref = oracle.moe_ffn(xh, ids, wts, g, u, dn, tokens=toks)
+            tot_s += time.perf_counter() - t1
+            tot_bytes += len(np.unique(ids[toks])) * sum(per_expert[l])
+            errs.append(assert_close(torch_bf16_bits(ys[l])[toks], yref, f"bench spot parity layer {l}"))
+            log(f"oracle layer {l}: {len(toks)} token(s) in {tot_s:.1f} s cumulative")
+        cpu = {"value": round(tot_bytes / tot_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{args.cpu_tokens} token(s) of layer(s) {sample_layers} "
+                         f"(CCQ and INT4 per-channel), all 8 routed experts decoded and multiplied; "
+                         f"{tot_bytes / 1e9:.3f} GB of packed weights in {tot_s:.1f} s"}
+        parity = max(errs)
+
+    out = {
+        "metric": "weight-stream HBM GB/s (decode M<=32), w2/w4 MoE stack",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random packed codes/scales, N(0,1) activations, uniform top-8 routing)",
+        "config": {"workload": "moe_stack_decode", "layers": L, "int4_per_channel_layers": n4,
+                   "ccq_g64_layers": L - n4, "experts": E, "topk": K, "hidden": H, "inter": I,
+                   "tokens": T, "resident_weight_bytes": resident,
+                   "step_weight_bytes": step_weight_bytes, "step_activation_bytes": step_act_bytes},
+        "tokens_per_s": round(tok_s, 2),
+        "roofline": {"kernel": "skinny_kernel CCQ gate+up (MODE_GATEUP)", "bound": "hbm",
+                     "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(gu_avg_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(gu_bytes)},
+        "cpu_baseline": cpu,
+        "spot_parity_max_rel_err": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -123,6 +123,22 @@ wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t
                      const wq_weight* up, const wq_weight* down, uint16_t* y, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* The stages of wq_moe_ffn, for callers that route elsewhere or time the stages separately
+ * (wq_moe_ffn = wq_moe_route + wq_moe_gate_up + wq_moe_down + wq_moe_combine).  The routing
+ * arrays are those wq_moe_route produces; npairs = t * topk.
+ * wq_moe_gate_up: h[r] = bf16(SiLU(W_gate[e] x_tok) * (W_up[e] x_tok)) for every sorted
+ *   position r (expert e, pair p = sorted_pairs[r], token p / topk); h bf16 [npairs][inter].
+ * wq_moe_down: d[p] = W_down[e] h[r] in fp32 for every sorted position r, stored by pair id
+ *   p = sorted_pairs[r]; d f32 [npairs][hidden].
+ * wq_moe_combine: y[t] = bf16(sum_j topk_weights[t][j] * d[t*topk + j]) (fp32, j in order). */
+wq_status wq_moe_gate_up(const uint16_t* x, int64_t t, const int32_t* expert_offsets,
+                         const int32_t* sorted_pairs, int32_t topk, const wq_weight* gate,
+                         const wq_weight* up, uint16_t* h, void* stream);
+wq_status wq_moe_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* expert_offsets,
+                      const int32_t* sorted_pairs, const wq_weight* down, float* d, void* stream);
+wq_status wq_moe_combine(const float* d, const float* topk_weights, int64_t t, int32_t topk,
+                         int64_t hidden, uint16_t* y, void* stream);
+
 /* Host helpers for the INT4 storage format (lesson E6.4, "Do it in code"); host memory.
  * wq_pack_int4: two codes per byte, the first in the low nibble, an odd count padded with 0;
  *   out must hold (n+1)/2 bytes; WQ_ERR_RANGE (nothing written) for a code outside -8..7.

@@ -221,3 +221,22 @@ def test_moe_all_tokens_one_expert(wq):
     y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
                       torch.from_numpy(wts).cuda(), to_device(gate), to_device(up), to_device(down))
     assert_close(torch_bf16_bits(y), ref, "moe one expert")
+
+
+def test_moe_stages_compose_to_ffn(wq):
+    # route + gate/up + down + combine called one by one give the bits of wq_moe_ffn
+    import torch
+
+    E, H, I, T, topk = 8, 512, 192, 20, 4
+    gate = to_device(_quant(oracle.CCQ, (E, I, H), (14, 1)))
+    up = to_device(_quant(oracle.CCQ, (E, I, H), (14, 2)))
+    down = to_device(_quant(oracle.CCQ, (E, H, I), (14, 3)))
+    x = torch.from_numpy(synth.acts_bf16((T, H), 15).view(np.int16)).cuda()
+    ids, wts = synth.routing_uniform(T, topk, E, 16)
+    ids_d, wts_d = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+    y_ffn = torch_bf16_bits(wq.wq_moe_ffn(x, ids_d, wts_d, gate, up, down))
+    off, pairs = wq.wq_moe_route(ids_d, E)
+    h = wq.wq_moe_gate_up(x, off, pairs, topk, gate, up)
+    d = wq.wq_moe_down(h, T, topk, off, pairs, down)
+    y = torch_bf16_bits(wq.wq_moe_combine(d, wts_d))
+    assert np.array_equal(y, y_ffn)

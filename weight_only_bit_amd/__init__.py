@@ -30,8 +30,8 @@ FMT_INT4, FMT_INT2_AFFINE, FMT_CCQ2 = 1, 2, 3
 
 # Every symbol include/wq.h declares.
 EXPORTS = ("wq_dequantize", "wq_gemm", "wq_moe_workspace_bytes", "wq_moe_route", "wq_moe_ffn",
-           "wq_pack_int4", "wq_unpack_int4", "wq_packed_size", "wq_status_string",
-           "wq_last_error")
+           "wq_moe_gate_up", "wq_moe_down", "wq_moe_combine", "wq_pack_int4", "wq_unpack_int4",
+           "wq_packed_size", "wq_status_string", "wq_last_error")
 
 
 class WqError(RuntimeError):
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
             "wq_moe_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
             "wq_moe_route": (i32, [vp, i64, i32, i32, vp, vp, vp, sz, vp]),
             "wq_moe_ffn": (i32, [vp, i64, i64, vp, vp, i32, W, W, W, vp, vp, sz, vp]),
+            "wq_moe_gate_up": (i32, [vp, i64, vp, vp, i32, W, W, vp, vp]),
+            "wq_moe_down": (i32, [vp, i64, i32, vp, vp, W, vp, vp]),
+            "wq_moe_combine": (i32, [vp, vp, i64, i32, i64, vp, vp]),
             "wq_pack_int4": (i32, [vp, i64, vp]),
             "wq_unpack_int4": (i32, [vp, i64, vp]),
             "wq_packed_size": (i64, [i64, i32]),
@@ -218,6 +221,44 @@ def wq_moe_ffn(x, topk_ids, topk_weights, gate: PackedWeight, up: PackedWeight,
                             ctypes.byref(gate.cstruct()), ctypes.byref(up.cstruct()),
                             ctypes.byref(down.cstruct()), _ptr(y), _ptr(ws), ws.numel(),
                             _stream()), "wq_moe_ffn")
+    return y
+
+
+def wq_moe_gate_up(x, offsets, sorted_pairs, topk: int, gate: PackedWeight, up: PackedWeight,
+                   h=None):
+    """h [t*topk, inter] bf16 (rows in expert-sorted order) = SiLU(gate x) * (up x)."""
+    import torch
+
+    t = x.shape[0]
+    if h is None:
+        h = torch.empty((t * topk, gate.n), dtype=torch.bfloat16, device=x.device)
+    _check(lib().wq_moe_gate_up(_ptr(x), t, _ptr(offsets), _ptr(sorted_pairs), topk,
+                                ctypes.byref(gate.cstruct()), ctypes.byref(up.cstruct()), _ptr(h),
+                                _stream()), "wq_moe_gate_up")
+    return h
+
+
+def wq_moe_down(h, t: int, topk: int, offsets, sorted_pairs, down: PackedWeight, d=None):
+    """d [t*topk, hidden] f32 (row = pair id) = down h."""
+    import torch
+
+    if d is None:
+        d = torch.empty((t * topk, down.n), dtype=torch.float32, device=h.device)
+    _check(lib().wq_moe_down(_ptr(h), t, topk, _ptr(offsets), _ptr(sorted_pairs),
+                             ctypes.byref(down.cstruct()), _ptr(d), _stream()), "wq_moe_down")
+    return d
+
+
+def wq_moe_combine(d, topk_weights, y=None):
+    """y [t, hidden] bf16 = sum_j topk_weights[t, j] * d[t*topk + j]."""
+    import torch
+
+    t, topk = topk_weights.shape
+    hidden = d.shape[1]
+    if y is None:
+        y = torch.empty((t, hidden), dtype=torch.bfloat16, device=d.device)
+    _check(lib().wq_moe_combine(_ptr(d), _ptr(topk_weights), t, topk, hidden, _ptr(y), _stream()),
+           "wq_moe_combine")
     return y
 
 

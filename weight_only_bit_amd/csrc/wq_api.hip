@@ -233,67 +233,143 @@ wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t
                     "wq_moe_route launch");
 }
 
+namespace {
+
+// Shared checks of the gate/up pair and the down matrix of one MoE layer.
+wq_status check_moe_weights(const wq_weight* gate, const wq_weight* up, const wq_weight* down,
+                            const char* what) {
+  wq_status st;
+  if (gate && (st = check_weight(gate, what)) != WQ_OK) return st;
+  if (up && (st = check_weight(up, what)) != WQ_OK) return st;
+  if (down && (st = check_weight(down, what)) != WQ_OK) return st;
+  if (gate && (st = check_product_zp(gate, what)) != WQ_OK) return st;
+  if (down && (st = check_product_zp(down, what)) != WQ_OK) return st;
+  const wq_weight* any = gate ? gate : down;
+  if (any->experts > kMaxExperts) return fail(WQ_ERR_UNSUPPORTED, "%s: at most %d experts", what, kMaxExperts);
+  if (gate && up) {
+    if (up->experts != gate->experts || up->n != gate->n || up->k != gate->k)
+      return fail(WQ_ERR_ARG, "%s: gate and up must both be [E][inter][hidden]", what);
+    if (gate->format != up->format || gate->group != up->group || gate->zp != up->zp)
+      return fail(WQ_ERR_UNSUPPORTED, "%s: gate and up must share format, group and zp", what);
+  }
+  if (gate && down && (down->experts != gate->experts || down->n != gate->k || down->k != gate->n))
+    return fail(WQ_ERR_ARG, "%s: down must be [E][hidden][inter] for gate/up [E][inter][hidden]", what);
+  return WQ_OK;
+}
+
+int moe_row_tiles(int64_t t, int32_t topk, int64_t experts) {
+  // 16 activation rows per pass while experts average at most 8 routed rows, else 32.
+  return ((double)t * topk / (double)experts <= 8.0) ? 1 : 2;
+}
+
+hipError_t run_gate_up(const uint16_t* x, int64_t t, const int32_t* offsets, const int32_t* sorted,
+                       int32_t topk, const wq_weight* gate, const wq_weight* up, uint16_t* h,
+                       hipStream_t s) {
+  wq::SkinnyArgs a{};
+  a.offsets = offsets;
+  a.sorted_pairs = sorted;
+  a.topk = topk;
+  a.w0 = dev_weight(gate);
+  a.w1 = dev_weight(up);
+  a.a = x;
+  a.a_stride = gate->k;
+  a.out = h;
+  a.out_stride = gate->n;
+  a.N = gate->n;
+  a.K = gate->k;
+  return wq::launch_skinny(gate->format, wq::MODE_GATEUP, moe_row_tiles(t, topk, gate->experts), 1,
+                           a, gate->experts, 1, s);
+}
+
+hipError_t run_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* offsets,
+                    const int32_t* sorted, const wq_weight* down, float* d, hipStream_t s) {
+  wq::SkinnyArgs a{};
+  a.offsets = offsets;
+  a.sorted_pairs = sorted;
+  a.topk = topk;
+  a.w0 = dev_weight(down);
+  a.w1 = a.w0;
+  a.a = h;
+  a.a_stride = down->k;
+  a.out = d;
+  a.out_stride = down->n;
+  a.N = down->n;
+  a.K = down->k;
+  return wq::launch_skinny(down->format, wq::MODE_DOWN, moe_row_tiles(t, topk, down->experts), 1,
+                           a, down->experts, 1, s);
+}
+
+}  // namespace
+
+wq_status wq_moe_gate_up(const uint16_t* x, int64_t t, const int32_t* expert_offsets,
+                         const int32_t* sorted_pairs, int32_t topk, const wq_weight* gate,
+                         const wq_weight* up, uint16_t* h, void* stream) {
+  if (!gate || !up) return fail(WQ_ERR_ARG, "wq_moe_gate_up: null descriptor");
+  wq_status st = check_moe_weights(gate, up, nullptr, "wq_moe_gate_up");
+  if (st != WQ_OK) return st;
+  if (t < 0 || topk <= 0) return fail(WQ_ERR_ARG, "wq_moe_gate_up: bad sizes");
+  if (t == 0) return WQ_OK;
+  if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_gate_up: too many pairs");
+  if (!x || !expert_offsets || !sorted_pairs || !h) return fail(WQ_ERR_ARG, "wq_moe_gate_up: null pointer");
+  if (!aligned16(x) || !aligned16(h)) return fail(WQ_ERR_ALIGN, "wq_moe_gate_up: x and h must be 16-byte aligned");
+  return hip_status(run_gate_up(x, t, expert_offsets, sorted_pairs, topk, gate, up, h,
+                                static_cast<hipStream_t>(stream)),
+                    "wq_moe_gate_up launch");
+}
+
+wq_status wq_moe_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* expert_offsets,
+                      const int32_t* sorted_pairs, const wq_weight* down, float* d, void* stream) {
+  if (!down) return fail(WQ_ERR_ARG, "wq_moe_down: null descriptor");
+  wq_status st = check_moe_weights(nullptr, nullptr, down, "wq_moe_down");
+  if (st != WQ_OK) return st;
+  if (t < 0 || topk <= 0) return fail(WQ_ERR_ARG, "wq_moe_down: bad sizes");
+  if (t == 0) return WQ_OK;
+  if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_down: too many pairs");
+  if (!h || !expert_offsets || !sorted_pairs || !d) return fail(WQ_ERR_ARG, "wq_moe_down: null pointer");
+  if (!aligned16(h) || !aligned16(d)) return fail(WQ_ERR_ALIGN, "wq_moe_down: h and d must be 16-byte aligned");
+  return hip_status(run_down(h, t, topk, expert_offsets, sorted_pairs, down, d,
+                             static_cast<hipStream_t>(stream)),
+                    "wq_moe_down launch");
+}
+
+wq_status wq_moe_combine(const float* d, const float* topk_weights, int64_t t, int32_t topk,
+                         int64_t hidden, uint16_t* y, void* stream) {
+  if (t < 0 || topk <= 0 || hidden <= 0) return fail(WQ_ERR_ARG, "wq_moe_combine: bad sizes");
+  if (hidden % 4 != 0) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_combine: hidden must be a multiple of 4");
+  if (t == 0) return WQ_OK;
+  if (!d || !topk_weights || !y) return fail(WQ_ERR_ARG, "wq_moe_combine: null pointer");
+  if (!aligned16(d) || !aligned16(y)) return fail(WQ_ERR_ALIGN, "wq_moe_combine: d and y must be 16-byte aligned");
+  return hip_status(wq::launch_combine(d, topk_weights, t, topk, hidden, y, static_cast<hipStream_t>(stream)),
+                    "wq_moe_combine launch");
+}
+
 wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
                      const float* topk_weights, int32_t topk, const wq_weight* gate,
                      const wq_weight* up, const wq_weight* down, uint16_t* y, void* ws,
                      size_t ws_bytes, void* stream) {
-  wq_status st;
-  if ((st = check_weight(gate, "wq_moe_ffn gate")) != WQ_OK) return st;
-  if ((st = check_weight(up, "wq_moe_ffn up")) != WQ_OK) return st;
-  if ((st = check_weight(down, "wq_moe_ffn down")) != WQ_OK) return st;
-  if ((st = check_product_zp(gate, "wq_moe_ffn gate")) != WQ_OK) return st;
-  if ((st = check_product_zp(down, "wq_moe_ffn down")) != WQ_OK) return st;
+  if (!gate || !up || !down) return fail(WQ_ERR_ARG, "wq_moe_ffn: null descriptor");
+  wq_status st = check_moe_weights(gate, up, down, "wq_moe_ffn");
+  if (st != WQ_OK) return st;
   if (t < 0 || topk <= 0 || hidden <= 0) return fail(WQ_ERR_ARG, "wq_moe_ffn: bad sizes");
-  const int64_t E = gate->experts, I = gate->n;
-  if (up->experts != E || down->experts != E)
-    return fail(WQ_ERR_ARG, "wq_moe_ffn: gate, up and down must have the same expert count");
-  if (E > kMaxExperts) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: at most %d experts", kMaxExperts);
-  if (gate->k != hidden || up->k != hidden || up->n != I || down->n != hidden || down->k != I)
-    return fail(WQ_ERR_ARG, "wq_moe_ffn: shapes must be gate/up [E][inter][hidden], down [E][hidden][inter]");
-  if (gate->format != up->format || gate->group != up->group || gate->zp != up->zp)
-    return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: gate and up must share format, group and zp");
+  if (gate->k != hidden) return fail(WQ_ERR_ARG, "wq_moe_ffn: gate/up k must equal hidden");
   if (hidden % 4 != 0) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: hidden must be a multiple of 4");
   if (t == 0) return WQ_OK;
   if (!x || !topk_ids || !topk_weights || !y || !ws) return fail(WQ_ERR_ARG, "wq_moe_ffn: null pointer");
   if (!aligned16(x) || !aligned16(y) || !aligned16(ws))
     return fail(WQ_ERR_ALIGN, "wq_moe_ffn: x, y and ws must be 16-byte aligned");
   if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: too many pairs");
+  const int64_t E = gate->experts, I = gate->n;
   MoeWs L = moe_layout(ws, t, topk, (int32_t)E, hidden, I);
   if (ws_bytes < L.bytes)
     return fail(WQ_ERR_WORKSPACE, "wq_moe_ffn: workspace %zu < %zu bytes", ws_bytes, L.bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = wq::launch_route(topk_ids, t * topk, (int32_t)E, L.offsets, L.sorted, s);
   if (e != hipSuccess) return hip_status(e, "wq_moe_ffn route");
-
-  wq::SkinnyArgs a{};
-  a.offsets = L.offsets;
-  a.sorted_pairs = L.sorted;
-  a.topk = topk;
-  // gate + up -> h (bf16, rows in expert-sorted order)
-  a.w0 = dev_weight(gate);
-  a.w1 = dev_weight(up);
-  a.a = x;
-  a.a_stride = hidden;
-  a.out = L.h;
-  a.out_stride = I;
-  a.N = I;
-  a.K = hidden;
-  const int mt = ((double)t * topk / (double)E <= 8.0) ? 1 : 2;
-  e = wq::launch_skinny(gate->format, wq::MODE_GATEUP, mt, 1, a, E, 1, s);
+  e = run_gate_up(x, t, L.offsets, L.sorted, topk, gate, up, L.h, s);
   if (e != hipSuccess) return hip_status(e, "wq_moe_ffn gate/up");
-  // down -> d (f32, rows indexed by pair id)
-  a.w0 = dev_weight(down);
-  a.w1 = a.w0;
-  a.a = L.h;
-  a.a_stride = I;
-  a.out = L.d;
-  a.out_stride = hidden;
-  a.N = hidden;
-  a.K = I;
-  e = wq::launch_skinny(down->format, wq::MODE_DOWN, mt, 1, a, E, 1, s);
+  e = run_down(L.h, t, topk, L.offsets, L.sorted, down, L.d, s);
   if (e != hipSuccess) return hip_status(e, "wq_moe_ffn down");
-  e = wq::launch_combine(L.d, topk_weights, t, topk, hidden, y, s);
-  return hip_status(e, "wq_moe_ffn combine");
+  return hip_status(wq::launch_combine(L.d, topk_weights, t, topk, hidden, y, s), "wq_moe_ffn combine");
 }
 
 }  // extern "C"
