@@ -35,9 +35,13 @@ wq_status hip_status(hipError_t e, const char* what) {
 
 // The product kernels decode CCQ weights as fma(u, s, -zp*s), exact when zp*s is exact: zp
 // must then be zero or a power of two (the format's zero point is 32).
+// The product kernels also address one expert's matrix with 32-bit byte offsets.
 wq_status check_product_zp(const wq_weight* w, const char* what) {
   if (w->format == WQ_FMT_CCQ2 && (w->zp & (w->zp - 1)) != 0)
     return fail(WQ_ERR_UNSUPPORTED, "%s: products need a CCQ zero point of 0 or a power of two", what);
+  const int64_t row_bytes = (w->format == WQ_FMT_INT4) ? w->k / 2 : w->k / 4;
+  if (w->n * row_bytes >= (1ll << 31))
+    return fail(WQ_ERR_UNSUPPORTED, "%s: one expert's codes must be below 2 GiB", what);
   return WQ_OK;
 }
 

@@ -2,17 +2,25 @@
 //
 // Every packed weight byte is read from HBM once per pass and decoded in registers straight
 // into MFMA B-operand fragments (exact bf16 weights, see wq_device.hpp); nothing decoded goes
-// through LDS or memory.
+// through LDS or memory.  The decode is VALU work (about 4.5 instructions per CCQ weight), so
+// the layout aims at keeping every SIMD's VALU busy:
 //
-// Work layout (one workgroup = 4 waves of 64):
-//   * a wave owns a 16-row tile of output channels (n) and, with KSPLIT = 4, a quarter of K;
-//   * the activation rows (16 or 32) are staged in LDS in 512-column chunks, double-buffered,
-//     shared by the 4 waves (16-byte row padding keeps the fragment reads conflict-free);
-//   * packed codes and group scales of the next chunk are prefetched into registers while the
-//     current chunk is multiplied;
-//   * per 64-weight group a lane decodes 16 weights of its row (one CCQ dword, two INT4 dwords
-//     or one 2-bit dword) into two 8-value B fragments and issues two 16x16x32 MFMAs per
-//     16-row activation tile; fp32 accumulation; one bf16 rounding in the epilogue.
+//   * one workgroup = 4 waves of 64; each wave decodes ONE weight matrix for a 16-row tile of
+//     output channels (MoE gate+up: two waves take gate tiles, two take the matching up tiles;
+//     their results meet in LDS for the SiLU(gate) * up epilogue);
+//   * packed codes and group scales are read with buffer loads from a per-wave resource (the
+//     lane's row offset is computed once; the step offset is a scalar), one chunk ahead of the
+//     decode.  Each lane loads 16 contiguous bytes of its row per step -- one 64-weight group
+//     of 2-bit codes or half a group of INT4 -- and the 4 lanes of a row take consecutive
+//     pieces, so a wave's load covers 64 contiguous bytes of each of its 16 rows and a lane
+//     needs one group scale per step.  (With exact bf16 weights the MFMA k-slots need not
+//     follow group boundaries.)
+//   * the activation rows (16 or 32) are staged in LDS in 512-column chunks, double-buffered
+//     and shared by the 4 waves; a 16-byte row pad keeps the A-fragment reads conflict-free;
+//   * per step a lane decodes its 64 (INT4: 32) weights 16 at a time into 8-value B fragments,
+//     each feeding one 16x16x32 MFMA per 16-row activation tile; fp32 accumulation, one bf16
+//     rounding in the epilogue;
+//   * dense products with few output tiles split K over the 4 waves (summed in LDS, in order).
 #include <hip/hip_runtime.h>
 
 #include "wq_kernels.hpp"
@@ -20,171 +28,160 @@
 namespace wq {
 namespace {
 
-constexpr int KCT = 512;  // activation columns per LDS chunk (all K-parts together)
+constexpr int KCT_BASE = 512;  // activation columns per LDS chunk (all K-parts together)
+constexpr int FMT_INT4PC = 4;  // INT4 with one scale per output channel (kernel variant)
 
+__host__ __device__ constexpr bool is_int4(int f) { return f == FMT_INT4 || f == FMT_INT4PC; }
+
+// Weights one lane decodes per step: 16 bytes of codes.
 template <int FMT>
-struct Raw;  // packed bytes + group metadata of one 64-weight group, one lane
-template <>
-struct Raw<FMT_INT4> {
-  u32x2 codes;
-  uint32_t scale;
-};
-template <>
-struct Raw<FMT_AFFINE2> {
-  uint32_t codes;
-  uint32_t scale;
-  uint32_t zero;
-};
-template <>
-struct Raw<FMT_CCQ2> {
-  uint32_t codes;
-  uint32_t qs;
-};
+__host__ __device__ constexpr int lane_weights() { return is_int4(FMT) ? 32 : 64; }
 
-// Per-lane, per-matrix row constants.
-struct RowConst {
-  const uint8_t* codes;    // row start
-  const uint16_t* scales;  // row start (INT4 g64 / AFFINE)
-  const uint8_t* zeros;    // row start (AFFINE)
-  const uint8_t* qscale;   // row start (CCQ)
-  float cs, cz;            // CCQ code scale / zero
-  float fin;               // CCQ super scale / INT4 per-channel scale (else 1)
-};
-
-__device__ __forceinline__ DevWeight at_expert(const DevWeight& w, int fmt, int64_t e) {
-  DevWeight r = w;
-  const int64_t G = w.k / 64;
-  const int64_t rows = e * w.n;
-  if (fmt == FMT_INT4) {
-    r.codes = w.codes + rows * (w.k / 2);
-    r.scales = w.scales + (w.group ? rows * G : rows);
-  } else if (fmt == FMT_AFFINE2) {
-    r.codes = w.codes + rows * (w.k / 4);
-    r.scales = w.scales + rows * G;
-    r.zeros = w.zeros + rows * G;
-  } else {
-    r.codes = w.codes + rows * (w.k / 4);
-    r.qscale = w.qscale + rows * ((G + 1) / 2);
-    r.super_scale = w.super_scale + rows;
-    r.code_scale = w.code_scale + rows;
-    r.code_zero = w.code_zero + rows;
-  }
-  return r;
+// Columns per wave per LDS chunk: at least one step (4 lanes x lane_weights).
+template <int FMT, int KSPLIT>
+__host__ __device__ constexpr int chunk_cols() {
+  return (KCT_BASE / KSPLIT) > 4 * lane_weights<FMT>() ? KCT_BASE / KSPLIT : 4 * lane_weights<FMT>();
 }
 
+// Packed data of one step for one lane: 16 bytes of its row and its group's scale.
 template <int FMT>
-__device__ __forceinline__ RowConst row_const(const DevWeight& w, int64_t row) {
-  RowConst c;
-  const int64_t G = w.k / 64;
-  c.cs = 0.f;
-  c.cz = 0.f;
-  c.fin = 1.0f;
-  c.scales = nullptr;
-  c.zeros = nullptr;
-  c.qscale = nullptr;
-  if (FMT == FMT_INT4) {
-    c.codes = w.codes + row * (w.k / 2);
-    if (w.group)
-      c.scales = w.scales + row * G;
-    else
-      c.fin = bf16_bits_to_f32(w.scales[row]);
-  } else if (FMT == FMT_AFFINE2) {
-    c.codes = w.codes + row * (w.k / 4);
-    c.scales = w.scales + row * G;
-    c.zeros = w.zeros + row * G;
-  } else {
-    c.codes = w.codes + row * (w.k / 4);
-    c.qscale = w.qscale + row * ((G + 1) / 2);
-    c.cs = w.code_scale[row];
-    c.cz = w.code_zero[row];
-    c.fin = w.super_scale[row];
-  }
-  return c;
+struct Raw {
+  u32x4 codes;
+  uint32_t scale;  // CCQ: the byte holding the 4-bit group scale; INT4 g64 / affine: bf16 bits
+  uint32_t zero;   // affine zero point
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// Load one group's packed data for this lane: weights k0 + 16*kb .. +15 of its row.
+// Per-wave view of one weight matrix (one expert); loads go through buffer resources, so an
+// offset outside the matrix reads zeros instead of faulting.
 template <int FMT>
-__device__ __forceinline__ void load_raw(Raw<FMT>& r, const RowConst& c, int64_t k0, int kb,
-                                         bool per_channel) {
-  const int64_t g = k0 >> 6;
-  if constexpr (FMT == FMT_INT4) {
-    r.codes = *reinterpret_cast<const u32x2*>(c.codes + (k0 >> 1) + kb * 8);
-    r.scale = per_channel ? 0u : (uint32_t)c.scales[g];
+struct WaveW {
+  __amdgpu_buffer_rsrc_t codes, scales, zeros;
+  int32_t row_codes;   // byte offset of this lane's row and 16-weight slice in codes
+  int32_t row_scales;  // byte offset of this lane's row in scales / qscale
+  int32_t row_zeros;
+  uint32_t qshift;     // CCQ: 0 or 4, the nibble of the scale byte that is this lane's group
+  float cs, cz;        // CCQ code scale / code zero of this lane's row
+  float fin;           // CCQ super scale / INT4 per-channel scale of this lane's row
+};
+
+// gb: first group of the wave's K range (its steps start at k = 64 gb).
+template <int FMT>
+__device__ __forceinline__ WaveW<FMT> wave_weight(const DevWeight& w, int64_t e, int64_t row,
+                                                  int kb, int32_t gb) {
+  WaveW<FMT> v;
+  const int64_t n = w.n, k = w.k, G = k / 64;
+  v.qshift = 0;
+  v.cs = v.cz = 0.f;
+  v.fin = 1.0f;
+  v.row_scales = v.row_zeros = 0;
+  v.zeros = v.scales = make_rsrc(w.codes, 0);
+  if constexpr (is_int4(FMT)) {
+    v.codes = make_rsrc(w.codes + e * n * (k / 2), n * (k / 2));
+    v.row_codes = (int32_t)(row * (k / 2) + gb * 32 + kb * 16);
+    if constexpr (FMT == FMT_INT4) {  // lane kb's 32 weights of step j lie in group gb + 2 j + kb / 2
+      v.scales = make_rsrc(w.scales + e * n * G, n * G * 2);
+      v.row_scales = (int32_t)(row * G * 2 + (gb + (kb >> 1)) * 2);
+    } else {
+      v.fin = bf16_bits_to_f32(w.scales[e * n + row]);
+    }
   } else if constexpr (FMT == FMT_AFFINE2) {
-    r.codes = *reinterpret_cast<const uint32_t*>(c.codes + (k0 >> 2) + kb * 4);
-    r.scale = c.scales[g];
-    r.zero = c.zeros[g];
+    v.codes = make_rsrc(w.codes + e * n * (k / 4), n * (k / 4));
+    v.row_codes = (int32_t)(row * (k / 4) + gb * 16 + kb * 16);  // group gb + 4 j + kb
+    v.scales = make_rsrc(w.scales + e * n * G, n * G * 2);
+    v.row_scales = (int32_t)(row * G * 2 + (gb + kb) * 2);
+    v.zeros = make_rsrc(w.zeros + e * n * G, n * G);
+    v.row_zeros = (int32_t)(row * G + gb + kb);
   } else {
-    r.codes = *reinterpret_cast<const uint32_t*>(c.codes + (k0 >> 2) + kb * 4);
-    r.qs = c.qscale[g >> 1];
+    const int64_t qb = (G + 1) / 2;
+    v.codes = make_rsrc(w.codes + e * n * (k / 4), n * (k / 4));
+    v.row_codes = (int32_t)(row * (k / 4) + gb * 16 + kb * 16);  // group gb + 4 j + kb
+    v.scales = make_rsrc(w.qscale + e * n * qb, n * qb);
+    v.row_scales = (int32_t)(row * qb + ((gb + kb) >> 1));  // two 4-bit scales per byte
+    v.qshift = 4u * (uint32_t)((gb + kb) & 1);
+    v.cs = w.code_scale[e * n + row];
+    v.cz = w.code_zero[e * n + row];
+    v.fin = w.super_scale[e * n + row];
+  }
+  return v;
+}
+
+// Load step st of the wave's K range (k = 64 gb + st * 4 * lane_weights) for this lane's row.
+// st is wave-uniform and goes in the scalar offset.
+template <int FMT>
+__device__ __forceinline__ void load_raw(Raw<FMT>& r, const WaveW<FMT>& v, int32_t st) {
+  r.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v.codes, v.row_codes, st * 64, 0));
+  if constexpr (FMT == FMT_INT4) {
+    r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 4, 0);
+  } else if constexpr (FMT == FMT_AFFINE2) {
+    r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 8, 0);
+    r.zero = __builtin_amdgcn_raw_buffer_load_b8(v.zeros, v.row_zeros, st * 4, 0);
+  } else if constexpr (FMT == FMT_CCQ2) {
+    r.scale = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.row_scales, st * 2, 0);
   }
 }
 
-template <int FMT, int MT, int NWN, int KSPLIT, int MODE>
+template <int FMT, int MT, int MODE, int KSPLIT>
 __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
-  constexpr int KCW = KCT / KSPLIT;  // columns per wave per chunk
-  constexpr int GPC = KCW / 64;      // groups per wave per chunk
+  constexpr int WPL = lane_weights<FMT>();     // weights per lane per step
+  constexpr int SSK = 4 * WPL;                 // k per step
+  constexpr int KCW = chunk_cols<FMT, KSPLIT>();  // columns per wave per chunk
+  constexpr int KCT = KCW * KSPLIT;
+  constexpr int SPC = KCW / SSK;               // steps per wave per chunk
   constexpr int ROWS = MT * 16;
-  constexpr int PITCH = KCT * 2 + 16;  // bytes per LDS row (16 B pad: conflict-free reads)
-  constexpr int NMAT = (MODE == MODE_GATEUP) ? 2 : 1;
-  constexpr int BLOCKS = ROWS * (KCT / 16);  // 16-element blocks per chunk
-  constexpr int BPT = BLOCKS / 256;          // blocks staged per thread
+  constexpr int PITCH = KCT * 2 + 16;  // bytes per LDS row
+  constexpr int BLOCKS = ROWS * (KCT / 16);
+  constexpr int BPT = BLOCKS / 256;  // 16-element activation blocks staged per thread
   static_assert(BPT * 256 == BLOCKS, "staging must divide evenly");
-  static_assert(NWN * KSPLIT == 4, "4 waves per workgroup");
+  static_assert(MODE == MODE_DENSE || KSPLIT == 1, "K split is for dense products");
+  constexpr int TPW = (KSPLIT == 4) ? 1 : (MODE == MODE_GATEUP ? 2 : 4);  // tiles per workgroup
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   uint8_t(*lds)[ROWS * PITCH] = reinterpret_cast<uint8_t(*)[ROWS * PITCH]>(lds_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave % NWN;
-  const int kw = wave / NWN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15;
   const int kb = lane >> 4;
+  const int kw = (KSPLIT == 4) ? wave : 0;
+  const int mat = (MODE == MODE_GATEUP) ? (wave >> 1) : 0;
+  const int tile_in_wg = (KSPLIT == 4) ? 0 : (MODE == MODE_GATEUP ? (wave & 1) : wave);
 
-  const int64_t N = args.N, K = args.K;
-  const int64_t Kpp = K / KSPLIT;
-  const int nchunks = (int)((Kpp + KCW - 1) / KCW);
+  const int64_t N = args.N;
+  const int32_t Kpp = (int32_t)(args.K / KSPLIT);  // K < 2^31 (checked on the host)
+  const int nchunks = (Kpp + KCW - 1) / KCW;
 
-  // Rows of this workgroup's activation block.
-  int64_t m_base, m_total;
+  int64_t m_base, m_total, e = 0;
   if constexpr (MODE == MODE_DENSE) {
     m_base = (int64_t)blockIdx.z * ROWS;
     m_total = args.M - m_base;
     if (m_total > ROWS) m_total = ROWS;
   } else {
-    const int e = blockIdx.y;
+    e = blockIdx.y;
     m_base = args.offsets[e];
     m_total = args.offsets[e + 1] - m_base;
     if (m_total <= 0) return;
   }
 
-  // Weights of this wave's 16-row tile.
-  DevWeight W0 = args.w0, W1 = args.w1;
-  if constexpr (MODE != MODE_DENSE) {
-    W0 = at_expert(args.w0, FMT, blockIdx.y);
-    if constexpr (NMAT == 2) W1 = at_expert(args.w1, FMT, blockIdx.y);
-  }
-  const int64_t n0 = ((int64_t)blockIdx.x * NWN + wn) * 16;
+  const int64_t n0 = ((int64_t)blockIdx.x * TPW + tile_in_wg) * 16;
   const int64_t nrow = n0 + nl;
   const bool nvalid = nrow < N;
   const int64_t nr = nvalid ? nrow : (N - 1);
-  RowConst rc[NMAT];
-  rc[0] = row_const<FMT>(W0, nr);
-  if constexpr (NMAT == 2) rc[1] = row_const<FMT>(W1, nr);
-  const bool per_channel = (FMT == FMT_INT4) && (W0.group == 0);
+  const int32_t g_part0 = (kw * Kpp) >> 6;  // first group of this wave's K part
+  const WaveW<FMT> W = wave_weight<FMT>(mat ? args.w1 : args.w0, e, nr, kb, g_part0);
+  const float zpf = (float)args.w0.zp;
 
-  const float zpf = (float)W0.zp;
-
-  // m super-tiles (one for dense; as many as the expert needs for MoE).
   for (int64_t ms = 0; ms < m_total; ms += ROWS) {
     const int64_t rows_here = (m_total - ms) < ROWS ? (m_total - ms) : ROWS;
 
-    // Source row pointers of the blocks this thread stages (fixed across chunks).
+    // Source rows of the activation blocks this thread stages (fixed across chunks).
     const uint16_t* srow[BPT];
-    int sblk[BPT];
-    int srowi[BPT];
+    int sblk[BPT], srowi[BPT];
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
       const int b = tid + 256 * i;
@@ -200,15 +197,14 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
           srow[i] = args.a + r * args.a_stride;
       }
     }
-
     u32x4 xr[BPT][2];
     auto stage_load = [&](int c) {
 #pragma unroll
       for (int i = 0; i < BPT; ++i) {
         const int part = sblk[i] / (KCW / 16);
-        const int64_t kin = (int64_t)c * KCW + (sblk[i] % (KCW / 16)) * 16;
+        const int32_t kin = c * KCW + (sblk[i] % (KCW / 16)) * 16;
         if (srow[i] != nullptr && kin < Kpp) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(srow[i] + part * Kpp + kin);
+          const u32x4* p = reinterpret_cast<const u32x4*>(srow[i] + (int64_t)part * Kpp + kin);
           xr[i][0] = p[0];
           xr[i][1] = p[1];
         } else {
@@ -226,75 +222,70 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
       }
     };
 
-    f32x4 acc[NMAT][MT];
+    f32x4 acc[MT];
 #pragma unroll
-    for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[q][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < MT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    Raw<FMT> rawA[NMAT][GPC], rawB[NMAT][GPC];
-    const int64_t kpart0 = (int64_t)kw * Kpp;
-    auto load_chunk = [&](Raw<FMT>(&r)[NMAT][GPC], int c) {
+    Raw<FMT> rawA[SPC], rawB[SPC];
+    auto load_chunk = [&](Raw<FMT>(&r)[SPC], int c) {
 #pragma unroll
-      for (int gi = 0; gi < GPC; ++gi) {
-        const int64_t kin = (int64_t)c * KCW + gi * 64;
-        if (kin < Kpp) {
-#pragma unroll
-          for (int q = 0; q < NMAT; ++q) load_raw<FMT>(r[q][gi], rc[q], kpart0 + kin, kb, per_channel);
-        }
-      }
+      for (int j = 0; j < SPC; ++j)
+        if (c * KCW + j * SSK < Kpp) load_raw<FMT>(r[j], W, c * SPC + j);
     };
-
-    auto compute_chunk = [&](Raw<FMT>(&r)[NMAT][GPC], int c, int buf) {
+    auto compute_chunk = [&](Raw<FMT>(&r)[SPC], int c, int buf) {
 #pragma unroll
-      for (int gi = 0; gi < GPC; ++gi) {
-        const int64_t kin = (int64_t)c * KCW + gi * 64;
-        if (kin >= Kpp) break;
-        // A fragments: rows t*16 + nl, block (kw part, group gi, kb), halves h
-        u32x4 A[MT][2];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const uint8_t* base = &lds[buf][(t * 16 + nl) * PITCH + (kw * (KCW / 16) + gi * 4 + kb) * 32];
-          A[t][0] = *reinterpret_cast<const u32x4*>(base);
-          A[t][1] = *reinterpret_cast<const u32x4*>(base + 16);
+      for (int j = 0; j < SPC; ++j) {
+        if (c * KCW + j * SSK >= Kpp) break;
+        const Raw<FMT>& rw = r[j];
+        float s = 1.0f, mzs = 0.0f;
+        if constexpr (FMT == FMT_CCQ2) {
+          s = (float)((rw.scale >> W.qshift) & 0xFu) * W.fin;
+          mzs = -zpf * s;
+        } else if constexpr (FMT == FMT_INT4) {
+          s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
+        } else if constexpr (FMT == FMT_INT4PC) {
+          s = W.fin;
+        } else {
+          s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
+          mzs = -(float)(rw.zero & 0xFFu) * s;
         }
+        // lane's A fragments: row t*16 + nl, columns kw*KCW + j*SSK + kb*WPL + 8h
+        const uint8_t* abase = &lds[buf][nl * PITCH + (kw * KCW + j * SSK + kb * WPL) * 2];
+        // 16 weights (two MFMAs) at a time
 #pragma unroll
-        for (int q = 0; q < NMAT; ++q) {
-          const Raw<FMT>& rw = r[q][gi];
+        for (int q = 0; q < WPL / 16; ++q) {
           uint32_t p[8];
           if constexpr (FMT == FMT_CCQ2) {
-            const int64_t g = (kpart0 + kin) >> 6;
-            const float s = (float)((rw.qs >> (4 * (g & 1))) & 0xFu) * rc[q].fin;
-            ccq_decode16(rw.codes, rc[q].cs, rc[q].cz, s, -zpf * s, p);
-          } else if constexpr (FMT == FMT_INT4) {
-            const float s = per_channel ? rc[q].fin : bf16_bits_to_f32(rw.scale);
-            int4_decode16(rw.codes.x, rw.codes.y, s, p);
+            ccq_decode16(rw.codes[q], W.cs, W.cz, s, mzs, p);
+          } else if constexpr (is_int4(FMT)) {
+            int4_decode16(rw.codes[2 * q], rw.codes[2 * q + 1], s, p);
           } else {
-            const float s = bf16_bits_to_f32(rw.scale);
-            affine2_decode16(rw.codes, s, -(float)rw.zero * s, p);
+            affine2_decode16(rw.codes[q], s, mzs, p);
           }
           const u32x4 B0 = {p[0], p[1], p[2], p[3]};
           const u32x4 B1 = {p[4], p[5], p[6], p[7]};
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
-            acc[q][t] = mfma16x16x32(A[t][0], B0, acc[q][t]);
-            acc[q][t] = mfma16x16x32(A[t][1], B1, acc[q][t]);
+            const u32x4 A0 = *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32);
+            const u32x4 A1 = *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32 + 16);
+            acc[t] = mfma16x16x32(A0, B0, acc[t]);
+            acc[t] = mfma16x16x32(A1, B1, acc[t]);
           }
         }
       }
     };
 
-    // Prologue: chunk 0's weights and activations.
     load_chunk(rawA, 0);
     stage_load(0);
     stage_store(0);
     __syncthreads();
-
-    auto step = [&](Raw<FMT>(&cur)[NMAT][GPC], Raw<FMT>(&nxt)[NMAT][GPC], int c, int buf) {
+    auto step = [&](Raw<FMT>(&cur)[SPC], Raw<FMT>(&nxt)[SPC], int c, int buf) {
       const bool more = (c + 1) < nchunks;
+      // Staging loads first: they are waited for at the end of this chunk, and vmcnt retires
+      // in order, so the weight loads issued after them stay in flight into the next chunk.
       if (more) {
-        load_chunk(nxt, c + 1);
         stage_load(c + 1);
+        load_chunk(nxt, c + 1);
       }
       compute_chunk(cur, c, buf);
       if (more) stage_store(buf ^ 1);
@@ -305,31 +296,40 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
       if (c + 1 < nchunks) step(rawB, rawA, c + 1, 1);
     }
 
-    // Sum the K-parts in order (waves kw = 1..KSPLIT-1 into kw = 0) through LDS.
+    // Results that meet in LDS: K parts summed in order (dense) or the up tile handed to the
+    // gate wave of the same tile (gate+up).
+    f32x4* red = reinterpret_cast<f32x4*>(&lds[0][0]);
     if constexpr (KSPLIT > 1) {
-      f32x4* red = reinterpret_cast<f32x4*>(&lds[0][0]);
       if (kw > 0) {
 #pragma unroll
-        for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-            red[(((kw - 1) * NWN + wn) * NMAT * MT + q * MT + t) * 64 + lane] = acc[q][t];
+        for (int t = 0; t < MT; ++t) red[((kw - 1) * MT + t) * 64 + lane] = acc[t];
       }
       __syncthreads();
       if (kw == 0) {
 #pragma unroll
         for (int p = 1; p < KSPLIT; ++p)
 #pragma unroll
-          for (int q = 0; q < NMAT; ++q)
+          for (int t = 0; t < MT; ++t) acc[t] += red[((p - 1) * MT + t) * 64 + lane];
+      }
+      __syncthreads();
+    }
+    f32x4 up[MT];
+    if constexpr (MODE == MODE_GATEUP) {
+      if (mat == 1) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-              acc[q][t] += red[(((p - 1) * NWN + wn) * NMAT * MT + q * MT + t) * 64 + lane];
+        for (int t = 0; t < MT; ++t) red[(tile_in_wg * MT + t) * 64 + lane] = acc[t];
+      }
+      __syncthreads();
+      if (mat == 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) up[t] = red[(tile_in_wg * MT + t) * 64 + lane];
       }
       __syncthreads();
     }
 
     // Epilogue: lane holds rows t*16 + 4*kb + i (i = 0..3) of column nrow.
-    if (kw == 0 && nvalid) {
+    const bool writer = (KSPLIT > 1) ? (kw == 0) : (mat == 0);
+    if (writer && nvalid) {
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -339,69 +339,71 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
           const int64_t r = m_base + ms + m;
           if constexpr (MODE == MODE_DENSE) {
             uint16_t* y = reinterpret_cast<uint16_t*>(args.out);
-            y[r * args.out_stride + nrow] = (uint16_t)f32_to_bf16_bits(acc[0][t][i]);
+            y[r * args.out_stride + nrow] = (uint16_t)f32_to_bf16_bits(acc[t][i]);
           } else if constexpr (MODE == MODE_GATEUP) {
-            const float gv = acc[0][t][i];
-            const float uv = acc[1][t][i];
             uint16_t* h = reinterpret_cast<uint16_t*>(args.out);
-            h[r * args.out_stride + nrow] = (uint16_t)f32_to_bf16_bits(silu_f32(gv) * uv);
+            h[r * args.out_stride + nrow] =
+                (uint16_t)f32_to_bf16_bits(silu_f32(acc[t][i]) * up[t][i]);
           } else {
             float* d = reinterpret_cast<float*>(args.out);
             const int64_t pair = args.sorted_pairs[r];
-            d[pair * args.out_stride + nrow] = acc[0][t][i];
+            d[pair * args.out_stride + nrow] = acc[t][i];
           }
         }
       }
     }
-    __syncthreads();
   }
 }
 
-template <int FMT, int MT, int NWN, int KSPLIT, int MODE>
+template <int FMT, int MT, int MODE, int KSPLIT>
 hipError_t launch_one(const SkinnyArgs& a, int64_t gy, int64_t gz, hipStream_t s) {
+  constexpr int KCT = chunk_cols<FMT, KSPLIT>() * KSPLIT;
   constexpr size_t lds_bytes = 2 * (size_t)(MT * 16) * (KCT * 2 + 16);
+  constexpr int TPW = (KSPLIT == 4) ? 1 : (MODE == MODE_GATEUP ? 2 : 4);
   static bool attr_set = false;  // per instantiation; the attribute is per-function state
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, NWN, KSPLIT, MODE>),
+        reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, MODE, KSPLIT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t ntiles = (a.N + 15) / 16;
-  dim3 grid((unsigned)((ntiles + NWN - 1) / NWN), (unsigned)gy, (unsigned)gz);
-  hipLaunchKernelGGL((skinny_kernel<FMT, MT, NWN, KSPLIT, MODE>), grid, dim3(256), lds_bytes, s, a);
+  dim3 grid((unsigned)((ntiles + TPW - 1) / TPW), (unsigned)gy, (unsigned)gz);
+  hipLaunchKernelGGL((skinny_kernel<FMT, MT, MODE, KSPLIT>), grid, dim3(256), lds_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int FMT, int MODE>
-hipError_t launch_fmt(int mt, int ksplit, const SkinnyArgs& a, int64_t gy, int64_t gz,
+template <int FMT>
+hipError_t launch_fmt(int mode, int mt, int ksplit, const SkinnyArgs& a, int64_t gy, int64_t gz,
                       hipStream_t s) {
-  if (ksplit == 4) {
-    if (mt == 1) return launch_one<FMT, 1, 1, 4, MODE>(a, gy, gz, s);
-    return launch_one<FMT, 2, 1, 4, MODE>(a, gy, gz, s);
+  if (mode == MODE_DENSE) {
+    if (ksplit == 4)
+      return mt == 1 ? launch_one<FMT, 1, MODE_DENSE, 4>(a, gy, gz, s)
+                     : launch_one<FMT, 2, MODE_DENSE, 4>(a, gy, gz, s);
+    return mt == 1 ? launch_one<FMT, 1, MODE_DENSE, 1>(a, gy, gz, s)
+                   : launch_one<FMT, 2, MODE_DENSE, 1>(a, gy, gz, s);
   }
-  if (mt == 1) return launch_one<FMT, 1, 4, 1, MODE>(a, gy, gz, s);
-  return launch_one<FMT, 2, 4, 1, MODE>(a, gy, gz, s);
-}
-
-template <int MODE>
-hipError_t launch_mode(int fmt, int mt, int ksplit, const SkinnyArgs& a, int64_t gy, int64_t gz,
-                       hipStream_t s) {
-  switch (fmt) {
-    case FMT_INT4: return launch_fmt<FMT_INT4, MODE>(mt, ksplit, a, gy, gz, s);
-    case FMT_AFFINE2: return launch_fmt<FMT_AFFINE2, MODE>(mt, ksplit, a, gy, gz, s);
-    default: return launch_fmt<FMT_CCQ2, MODE>(mt, ksplit, a, gy, gz, s);
-  }
+  if (mode == MODE_GATEUP)
+    return mt == 1 ? launch_one<FMT, 1, MODE_GATEUP, 1>(a, gy, gz, s)
+                   : launch_one<FMT, 2, MODE_GATEUP, 1>(a, gy, gz, s);
+  return mt == 1 ? launch_one<FMT, 1, MODE_DOWN, 1>(a, gy, gz, s)
+                 : launch_one<FMT, 2, MODE_DOWN, 1>(a, gy, gz, s);
 }
 
 }  // namespace
 
 hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
                          int64_t grid_y, int64_t grid_z, hipStream_t stream) {
-  if (mode == MODE_DENSE) return launch_mode<MODE_DENSE>(fmt, m_tiles, ksplit, args, grid_y, grid_z, stream);
-  if (mode == MODE_GATEUP) return launch_mode<MODE_GATEUP>(fmt, m_tiles, 1, args, grid_y, grid_z, stream);
-  return launch_mode<MODE_DOWN>(fmt, m_tiles, 1, args, grid_y, grid_z, stream);
+  switch (fmt) {
+    case FMT_INT4:
+      if (args.w0.group == 0)
+        return launch_fmt<FMT_INT4PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+      return launch_fmt<FMT_INT4>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_AFFINE2:
+      return launch_fmt<FMT_AFFINE2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    default: return launch_fmt<FMT_CCQ2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+  }
 }
 
 }  // namespace wq
