@@ -178,12 +178,15 @@ def test_route_exact(wq, t, topk, experts, kind):
 
 
 MOE_CASES = [
-    # name, E, hidden, inter, tokens, topk
+    # name, E, hidden, inter, tokens, topk  (avg rows per expert >= 32 runs the tiled kernels)
     ("ccq", 8, 256, 192, 5, 2),
     ("ccq", 8, 512, 320, 40, 4),
     ("int4pc", 6, 256, 128, 12, 3),
     ("affine2", 4, 256, 192, 9, 2),
     ("int4", 4, 192, 128, 70, 2),
+    ("ccq", 4, 256, 192, 64, 2),        # tiled, 32 rows per expert on average
+    ("int4pc", 8, 512, 320, 200, 4),    # tiled, ragged row tiles
+    ("affine2", 4, 320, 128, 96, 2),    # tiled
 ]
 
 
@@ -240,3 +243,46 @@ def test_moe_stages_compose_to_ffn(wq):
     d = wq.wq_moe_down(h, T, topk, off, pairs, down)
     y = torch_bf16_bits(wq.wq_moe_combine(d, wts_d))
     assert np.array_equal(y, y_ffn)
+
+
+def test_tiled_gemm_decodes_every_weight_bit_exact(wq):
+    # 128-row identity blocks go through the tiled kernel (more than 32 rows): y[m][n] =
+    # W_hat[n][c0 + m] exactly, for every weight, in every format.
+    import torch
+
+    for name in ("ccq", "int4", "int4pc", "affine2"):
+        fmt = FMTS["int4" if name == "int4pc" else name]
+        group = 0 if name == "int4pc" else 64
+        n, k = 136, 320
+        p = _quant(fmt, (n, k), (17, fmt, group), group=group)
+        ref = oracle.dequantize(p)
+        d = to_device(p)
+        for c0 in range(0, k, 128):
+            w = min(128, k - c0)
+            x = np.zeros((w, k), np.uint16)
+            x[np.arange(w), c0 + np.arange(w)] = 0x3F80
+            y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
+            assert np.array_equal(y.T, ref[:, c0:c0 + w]), f"{name} columns {c0}.."
+
+
+@pytest.mark.parametrize("name", ["ccq", "int4pc"])
+def test_moe_prefill_skewed_routing(wq, name):
+    # Zipf-biased routing as in the prefill workload, at reduced sizes: most rows go to the
+    # first experts (several 128-row tiles), the tail experts get a few rows or none.
+    import torch
+
+    fmt = FMTS["int4" if name == "int4pc" else name]
+    group = 0 if name == "int4pc" else 64
+    E, H, I, T, topk = 16, 512, 256, 384, 4
+    gate = _quant(fmt, (E, I, H), (18, 1), group=group)
+    up = _quant(fmt, (E, I, H), (18, 2), group=group)
+    down = _quant(fmt, (E, H, I), (18, 3), group=group)
+    x = synth.acts_bf16((T, H), 19)
+    ids, wts = synth.routing_zipf(T, topk, E, 20)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.max() > 128 and counts.min() < 32
+    tokens = np.array([0, 1, 2, 100, 200, 383], np.int32)
+    ref = oracle.moe_ffn(x, ids, wts, gate, up, down, tokens=tokens)
+    y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(wts).cuda(), to_device(gate), to_device(up), to_device(down))
+    assert_close(torch_bf16_bits(y)[tokens], ref, f"moe prefill {name}")

@@ -128,6 +128,10 @@ MoeWs moe_layout(void* ws, int64_t t, int32_t topk, int32_t experts, int64_t hid
 }
 
 constexpr int32_t kMaxExperts = 512;
+// Up to this many activation rows the decode-streaming kernels run; above it the tiled ones.
+constexpr int64_t kSkinnyMaxRows = 32;
+// MoE layers whose experts average at least this many routed rows use the tiled kernels.
+constexpr double kMoeTiledRows = 32.0;
 
 }  // namespace
 
@@ -196,6 +200,21 @@ wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y,
   if (!aligned16(x) || !aligned16(y)) return fail(WQ_ERR_ALIGN, "wq_gemm: x or y not 16-byte aligned");
   if (m > (1ll << 31)) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: m must be below 2^31");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m > kSkinnyMaxRows) {
+    wq::TiledArgs t{};
+    t.w0 = dev_weight(w);
+    t.w1 = t.w0;
+    t.a = x;
+    t.a_stride = w->k;
+    t.out = y;
+    t.out_stride = w->n;
+    t.M = m;
+    t.N = w->n;
+    t.K = w->k;
+    const int64_t bm = wq::tiled_rows();
+    return hip_status(wq::launch_tiled(w->format, wq::MODE_DENSE, t, (m + bm - 1) / bm, s),
+                      "wq_gemm launch");
+  }
   wq::SkinnyArgs a{};
   a.w0 = dev_weight(w);
   a.w1 = a.w0;
@@ -266,9 +285,40 @@ int moe_row_tiles(int64_t t, int32_t topk, int64_t experts) {
   return ((double)t * topk / (double)experts <= 8.0) ? 1 : 2;
 }
 
+bool moe_tiled(int64_t t, int32_t topk, int64_t experts) {
+  return (double)t * topk / (double)experts >= kMoeTiledRows;
+}
+
+int64_t moe_tile_bound(int64_t t, int32_t topk, int64_t experts) {
+  const int64_t bm = wq::tiled_rows();
+  return (t * topk + bm - 1) / bm + experts;
+}
+
+wq::TiledArgs moe_tiled_args(const int32_t* offsets, const int32_t* sorted, int32_t topk,
+                             int64_t experts) {
+  wq::TiledArgs a{};
+  a.offsets = offsets;
+  a.sorted_pairs = sorted;
+  a.topk = topk;
+  a.experts = (int32_t)experts;
+  return a;
+}
+
 hipError_t run_gate_up(const uint16_t* x, int64_t t, const int32_t* offsets, const int32_t* sorted,
                        int32_t topk, const wq_weight* gate, const wq_weight* up, uint16_t* h,
                        hipStream_t s) {
+  if (moe_tiled(t, topk, gate->experts)) {
+    wq::TiledArgs a = moe_tiled_args(offsets, sorted, topk, gate->experts);
+    a.w0 = dev_weight(gate);
+    a.w1 = dev_weight(up);
+    a.a = x;
+    a.a_stride = gate->k;
+    a.out = h;
+    a.out_stride = gate->n;
+    a.N = gate->n;
+    a.K = gate->k;
+    return wq::launch_tiled(gate->format, wq::MODE_GATEUP, a, moe_tile_bound(t, topk, gate->experts), s);
+  }
   wq::SkinnyArgs a{};
   a.offsets = offsets;
   a.sorted_pairs = sorted;
@@ -287,6 +337,18 @@ hipError_t run_gate_up(const uint16_t* x, int64_t t, const int32_t* offsets, con
 
 hipError_t run_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* offsets,
                     const int32_t* sorted, const wq_weight* down, float* d, hipStream_t s) {
+  if (moe_tiled(t, topk, down->experts)) {
+    wq::TiledArgs a = moe_tiled_args(offsets, sorted, topk, down->experts);
+    a.w0 = dev_weight(down);
+    a.w1 = a.w0;
+    a.a = h;
+    a.a_stride = down->k;
+    a.out = d;
+    a.out_stride = down->n;
+    a.N = down->n;
+    a.K = down->k;
+    return wq::launch_tiled(down->format, wq::MODE_DOWN, a, moe_tile_bound(t, topk, down->experts), s);
+  }
   wq::SkinnyArgs a{};
   a.offsets = offsets;
   a.sorted_pairs = sorted;

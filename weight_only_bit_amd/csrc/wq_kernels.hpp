@@ -40,28 +40,26 @@ hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int
 hipError_t launch_combine(const float* d, const float* weights, int64_t t, int32_t topk,
                           int64_t hidden, uint16_t* y, hipStream_t stream);
 
-// Arguments of the LDS-staged MFMA GEMM (large row counts).
+// Arguments of the LDS-staged MFMA GEMM (many activation rows).
 struct TiledArgs {
   DevWeight w0, w1;             // as SkinnyArgs
-  const uint16_t* a;
+  const uint16_t* a;            // activations (rows as in SkinnyArgs)
   int64_t a_stride;
   void* out;
   int64_t out_stride;
-  int64_t M, N, K;
-  const int32_t* offsets;
+  int64_t M, N, K;              // M: dense rows
+  const int32_t* offsets;       // MoE expert offsets [E+1]
   const int32_t* sorted_pairs;
   int32_t topk;
   int32_t experts;
-  const int32_t* tile_expert;   // MoE: per m-tile work item, its expert (device)
-  const int32_t* tile_row;      // MoE: per m-tile work item, its first row within the expert
-  const int32_t* tile_count;    // MoE: number of m-tile work items (device scalar)
 };
 
-hipError_t launch_tiled(int fmt, int mode, const TiledArgs& args, int64_t max_mtiles,
-                        hipStream_t stream);
+// Rows of one tile of the tiled kernel.
+int tiled_rows();
 
-hipError_t launch_tile_list(const int32_t* offsets, int32_t experts, int32_t bm,
-                            int32_t* tile_expert, int32_t* tile_row, int32_t* tile_count,
-                            hipStream_t stream);
+// row_tiles: dense: ceil(M / tiled_rows()); MoE: an upper bound of sum_e ceil(rows_e /
+// tiled_rows()) (extra workgroups exit).
+hipError_t launch_tiled(int fmt, int mode, const TiledArgs& args, int64_t row_tiles,
+                        hipStream_t stream);
 
 }  // namespace wq
