@@ -26,6 +26,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_ccq_gateup_moe_decode.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the CCQ gate+up kernel from the committed rocprofv3 counter
+    runs (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel sources
+    changed since those counters were taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["kernel_sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["kernel_sources_sha256"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -40,8 +61,13 @@ def parse():
     ap.add_argument("--layers", type=int, default=54, help="MoE layers in the stack")
     ap.add_argument("--int4-layers", type=int, default=7, help="leading INT4 per-channel layers")
     ap.add_argument("--tokens", type=int, default=32)
-    ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens per sampled layer for the CPU baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens per sampled layer for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="moe_stack_decode",
+                    choices=["moe_stack_decode", "moe_prefill", "dense_decode", "copy_calibration"],
+                    help="moe_stack_decode (default): the 54-layer stack step; moe_prefill: one "
+                         "CCQ MoE layer at 4096 tokens with Zipf-skewed routing; dense_decode: "
+                         "one 4096x4096 CCQ / 2-bit affine linear at 1, 8, 32 rows")
     return ap.parse_args()
 
 
@@ -78,6 +104,12 @@ def main():
               f"one device (no sharding, no collectives); got --gpus {args.gpus}, WORLD_SIZE {world}.",
               flush=True)
         sys.exit(2)
+    if args.workload == "moe_prefill":
+        return moe_prefill(args)
+    if args.workload == "dense_decode":
+        return dense_decode(args)
+    if args.workload == "copy_calibration":
+        return copy_calibration(args)
 
     import numpy as np
     import torch
@@ -219,13 +251,124 @@ def main():
         "tokens_per_s": round(tok_s, 2),
         "roofline": {"kernel": "skinny_kernel CCQ gate+up (MODE_GATEUP)", "bound": "hbm",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(gu_avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(gu_bytes)},
         "cpu_baseline": cpu,
         "spot_parity_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def moe_prefill(args):
+    """One CCQ MoE layer at prefill size: 4096 tokens, top-8 of 64 experts, Zipf(1.1)-biased
+    routing.  Reports unpadded bf16 TFLOP/s (2 * pairs * 3 * hidden * inter per call)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_only_bit_amd as wq
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    E, H, I, K, T = 64, 8192, 3584, 8, 4096
+    g, u, dn = make_layer(wq, synth, wq.FMT_CCQ2, E, H, I, 2000, 64)
+    x = torch.from_numpy(synth.acts_bf16((T, H), 501).view(np.int16)).to(dev)
+    ids, wts = synth.routing_zipf(T, K, E, 601)
+    ids_d, wts_d = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(wq.wq_moe_workspace_bytes(T, K, E, H, I), dtype=torch.uint8, device=dev)
+    flops = 2.0 * T * K * 3 * H * I
+    for _ in range(args.warmup):
+        wq.wq_moe_ffn(x, ids_d, wts_d, g, u, dn, y=y, ws=ws)
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(args.steps):
+        wq.wq_moe_ffn(x, ids_d, wts_d, g, u, dn, y=y, ws=ws)
+    en.record()
+    torch.cuda.synchronize()
+    ms = st.elapsed_time(en) / args.steps
+    tf = flops / (ms * 1e-3) / 1e12
+    counts = np.bincount(ids.ravel(), minlength=E)
+    out = {"metric": "bf16 TFLOP/s (prefill MoE layer, CCQ g64)", "value": round(tf, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "moe_prefill", "tokens": T, "topk": K, "experts": E,
+                      "hidden": H, "inter": I, "routing": "zipf s=1.1",
+                      "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())},
+           "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+    print(json.dumps(out), flush=True)
+
+
+def dense_decode(args):
+    """One 4096 x 4096 linear at 1, 8 and 32 rows, CCQ and 2-bit affine; each call reads one of
+    enough distinct weight copies (>= 1 GiB in total) that the 256 MB last-level cache holds no
+    weights between calls."""
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_only_bit_amd as wq
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    N = Kd = 4096
+    res = {}
+    for fmt, name in ((wq.FMT_CCQ2, "ccq"), (wq.FMT_INT2_AFFINE, "affine2")):
+        one = None
+        copies = []
+        for c in range(256):
+            arr = synth.random_packed_device(fmt, 1, N, Kd, 3000 + c)
+            w = wq.PackedWeight(fmt, N, Kd, 1, 64, *(arr.get(f) for f in (
+                "codes", "scales", "zeros", "qscale", "super_scale", "code_scale", "code_zero")), 32)
+            copies.append(w)
+            one = w.nbytes()
+            if one * len(copies) >= (1 << 30):
+                break
+        for m in (1, 8, 32):
+            x = torch.from_numpy(synth.acts_bf16((m, Kd), 502, m).view(np.int16)).to(dev)
+            y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            for i in range(len(copies)):
+                wq.wq_gemm(x, copies[i], y=y)
+            torch.cuda.synchronize()
+            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(args.steps, 1) * len(copies)
+            st.record()
+            for i in range(reps):
+                wq.wq_gemm(x, copies[i % len(copies)], y=y)
+            en.record()
+            torch.cuda.synchronize()
+            us = st.elapsed_time(en) / reps * 1e3
+            res[f"{name}_m{m}"] = {"us": round(us, 2), "GB/s": round(one / (us * 1e-6) / 1e9, 1)}
+    out = {"metric": "weight-stream GB/s, dense 4096x4096 linear", "value": res["ccq_m1"]["GB/s"],
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "dense_decode", "n": N, "k": Kd}, "results": res}
+    print(json.dumps(out), flush=True)
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of exactly 1 GiB (one dispatch per step): the reference
+    for scaling the FETCH_SIZE / WRITE_SIZE hardware counters to bytes."""
+    import torch
+
+    torch.cuda.set_device(0)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(max(args.steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copy_calibration", "bytes_read": n, "bytes_written": n,
+                      "copies": max(args.steps, 1)}), flush=True)
 
 
 if __name__ == "__main__":
