@@ -286,3 +286,31 @@ def test_moe_prefill_skewed_routing(wq, name):
     y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
                       torch.from_numpy(wts).cuda(), to_device(gate), to_device(up), to_device(down))
     assert_close(torch_bf16_bits(y)[tokens], ref, f"moe prefill {name}")
+
+
+def test_gemm_ccq_clamped_rows_bit_exact(wq):
+    # Rows whose code scale / zero push the expanded code below 0 or above 2^15 - 1 (and rows
+    # that stay inside, in the same 16-row tile): the product path's decode must still equal
+    # the oracle's bits (identity activations read the weights back).
+    import torch
+
+    rows, k = 32, 256
+    g = np.random.default_rng(23)
+    cs = np.tile(np.array([0.5, 1.5, 128.5, 127.25, 200.0, 300.0, 1.0, 64.0625,
+                           0.75, 2.5, 128.0, 129.0, 1e-3, 255.0, 128.49, 97.7], np.float32), 2)
+    cz = np.tile(np.array([0.5, -0.5, -100.0, 0.25, 0.0, -5.0, 32760.0, 10.5,
+                           -0.49, 0.5, 32767.0, -129.0, 0.5, 0.0, 1.5, 3.0], np.float32), 2)
+    codes = g.integers(0, 256, (1, rows, k // 4), dtype=np.uint8)
+    sq = g.integers(1, 16, (rows, k // 128), dtype=np.uint8)
+    p = oracle.Packed(oracle.CCQ, rows, k, 1, 64, codes, qscale=(sq | (sq << 4))[None],
+                      super_scale=np.full((1, rows), 3e-4, np.float32), code_scale=cs[None],
+                      code_zero=cz[None], zp=32)
+    ref = oracle.dequantize(p)
+    d = to_device(p)
+    for m in (32, 128):  # decode-streaming and tiled kernels
+        for c0 in range(0, k, m):
+            w = min(m, k - c0)
+            x = np.zeros((w, k), np.uint16)
+            x[np.arange(w), c0 + np.arange(w)] = 0x3F80
+            y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
+            assert np.array_equal(y.T, ref[:, c0:c0 + w]), (m, c0)

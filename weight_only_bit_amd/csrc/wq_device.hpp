@@ -59,10 +59,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 1.5 * 2^23 to a value in [0, 2^15) rounds it half-to-even to an integer that lands in the
 // low mantissa bits, so the returned float's bit pattern is 0x4B400000 + C: bits 0..14 are C.
 // ---------------------------------------------------------------------------------------------
+template <bool CLAMP = true>
 __device__ __forceinline__ uint32_t ccq_expand_bits(float cprime, float cscale, float czero) {
   float t = __builtin_fmaf(cprime, cscale, czero);
-  t = __builtin_amdgcn_fmed3f(t, 0.0f, 32767.0f);
+  if (CLAMP) t = __builtin_amdgcn_fmed3f(t, 0.0f, 32767.0f);
   return __float_as_uint(t + 12582912.0f);
+}
+
+// True when no byte of a row can expand outside [0, 32767] (so the clamp is the identity):
+// fmaf is monotonic in C', so checking C' = 0 and C' = 255 covers the row.
+__device__ __forceinline__ bool ccq_row_needs_no_clamp(float cscale, float czero) {
+  const float a = __builtin_fmaf(0.0f, cscale, czero), b = __builtin_fmaf(255.0f, cscale, czero);
+  return fminf(a, b) >= 0.0f && fmaxf(a, b) <= 32767.0f;
 }
 
 // Two fp32 values -> packed bf16 pair (round half to even), low half first.
@@ -84,11 +92,13 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // ---------------------------------------------------------------------------------------------
 
 // CCQ: one dword = 4 clustered bytes = 16 weights.  s = f32(s_q) * super, mzs = -zp * s.
+// CLAMP = false only when ccq_row_needs_no_clamp holds for the row.
+template <bool CLAMP = true>
 __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs, float cz, float s, float mzs,
                                              uint32_t (&p)[8]) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const uint32_t R = ccq_expand_bits((float)((w >> (8 * b)) & 0xFFu), cs, cz);
+    const uint32_t R = ccq_expand_bits<CLAMP>((float)((w >> (8 * b)) & 0xFFu), cs, cz);
     float f[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)  // bit-shift decode: shifts 9, 6, 3, 0; mask 0x3F
@@ -96,6 +106,14 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs, float cz, flo
     p[2 * b] = cvt_pk_bf16(f[0], f[1]);
     p[2 * b + 1] = cvt_pk_bf16(f[2], f[3]);
   }
+}
+
+// a & b, opaque to the optimizer: keeps a masked dword whole so each byte is converted by
+// one v_cvt_f32_ubyteN instead of a bit-field extract plus a convert.
+__device__ __forceinline__ uint32_t and_opaque(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // INT4: two dwords = 16 signed nibbles (first weight in the low nibble).  XOR 8 biases a
@@ -106,8 +124,8 @@ __device__ __forceinline__ void int4_decode16(uint32_t w0, uint32_t w1, float s,
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t d = (h ? w1 : w0) ^ 0x88888888u;
-    const uint32_t ev = d & 0x0F0F0F0Fu;         // nibbles 0,2,4,6 -> bytes 0..3
-    const uint32_t od = (d >> 4) & 0x0F0F0F0Fu;  // nibbles 1,3,5,7
+    const uint32_t ev = and_opaque(d, 0x0F0F0F0Fu);       // nibbles 0,2,4,6 -> bytes 0..3
+    const uint32_t od = and_opaque(d >> 4, 0x0F0F0F0Fu);  // nibbles 1,3,5,7
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const float a = __builtin_fmaf((float)((ev >> (8 * b)) & 0xFFu), s, m8s);
@@ -123,7 +141,7 @@ __device__ __forceinline__ void affine2_decode16(uint32_t w, float s, float mzs,
                                                  uint32_t (&p)[8]) {
   uint32_t q[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = (w >> (2 * i)) & 0x03030303u;  // byte b holds code 4b + i
+  for (int i = 0; i < 4; ++i) q[i] = and_opaque(w >> (2 * i), 0x03030303u);  // byte b: code 4b + i
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     float f[4];

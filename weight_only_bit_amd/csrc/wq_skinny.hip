@@ -23,6 +23,8 @@
 //   * dense products with few output tiles split K over the 4 waves (summed in LDS, in order).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "wq_kernels.hpp"
 
 namespace wq {
@@ -176,6 +178,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   const WaveW<FMT> W = wave_weight<FMT>(mat ? args.w1 : args.w0, e, nr, kb, g_part0);
   const float zpf = (float)args.w0.zp;
 
+  // CCQ rows whose codes can never leave [0, 2^15 - 1] skip the clamp (one instruction per
+  // byte); the choice is uniform over the wave.
+  bool no_clamp = false;
+  if constexpr (FMT == FMT_CCQ2) no_clamp = __all(ccq_row_needs_no_clamp(W.cs, W.cz));
+  auto run = [&](auto clamp_tag) {
+    constexpr bool CLAMP = decltype(clamp_tag)::value;
   for (int64_t ms = 0; ms < m_total; ms += ROWS) {
     const int64_t rows_here = (m_total - ms) < ROWS ? (m_total - ms) : ROWS;
 
@@ -256,7 +264,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
         for (int q = 0; q < WPL / 16; ++q) {
           uint32_t p[8];
           if constexpr (FMT == FMT_CCQ2) {
-            ccq_decode16(rw.codes[q], W.cs, W.cz, s, mzs, p);
+            ccq_decode16<CLAMP>(rw.codes[q], W.cs, W.cz, s, mzs, p);
           } else if constexpr (is_int4(FMT)) {
             int4_decode16(rw.codes[2 * q], rw.codes[2 * q + 1], s, p);
           } else {
@@ -353,6 +361,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
       }
     }
   }
+  };
+  if (no_clamp)
+    run(std::integral_constant<bool, false>{});
+  else
+    run(std::integral_constant<bool, true>{});
 }
 
 template <int FMT, int MT, int MODE, int KSPLIT>
