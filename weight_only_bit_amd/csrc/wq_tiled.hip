@@ -1,14 +1,16 @@
 // wq_tiled.hip -- weight-only GEMM for many activation rows (prefill): LDS-staged exact-bf16
 // weight tiles feeding bf16 MFMA.
 //
-// One workgroup = 4 waves computes a 128 (activation rows) x 128 (output channels) tile; K
+// One workgroup = 8 waves computes a 256 (activation rows) x 128 (output channels) tile; K
 // advances one 64-weight group per step.  Per step:
-//   * the packed codes of the 128 x 64 weight tile are decoded once, by all 256 threads, to
+//   * the packed codes of the 128 x 64 weight tile are decoded once, by all 512 threads, to
 //     the exact bf16 weights (the same bits wq_dequantize produces) and written to LDS; each
-//     decoded weight is then used by 128 activation rows;
-//   * the 128 x 64 bf16 activation tile is copied to LDS (gathered rows for MoE);
-//   * each wave multiplies a 64 x 64 quarter with v_mfma_f32_32x32x16_bf16 (2 x 2 tiles x 4
-//     k-steps), fp32 accumulation.
+//     decoded weight is then used by 256 activation rows -- enough reuse that the decode's
+//     VALU work (about 4.5 instructions per CCQ weight) stays below the MFMA time;
+//   * the 256 x 64 bf16 activation tile is copied to LDS (gathered rows for MoE);
+//   * each wave multiplies a 64 x 64 block with v_mfma_f32_32x32x16_bf16 (2 x 2 tiles x 4
+//     k-steps), fp32 accumulation; waves whose rows are all past the end of a ragged tile skip
+//     their MFMAs.
 // LDS is double-buffered: the next step's packed bytes and activations are loaded into
 // registers before the current MFMAs are issued, and decoded/stored after them, so the
 // decode's VALU work overlaps the matrix-core work.
@@ -24,16 +26,18 @@
 namespace wq {
 namespace {
 
-constexpr int BM = 128;            // activation rows per tile
+constexpr int BM = 256;            // activation rows per tile
 constexpr int BN = 128;            // weight rows (output channels) per tile
 constexpr int BK = 64;             // k per step (one group)
+constexpr int NTHREADS = 512;      // 8 waves: 4 along rows x 2 along channels
 constexpr int LPITCH = BK * 2 + 16;  // LDS row pitch in bytes (pad: conflict-free 16 B reads)
-constexpr int TILE_BYTES = 128 * LPITCH;
+constexpr int A_BYTES = BM * LPITCH;
+constexpr int B_BYTES = BN * LPITCH;
 
-// Packed bytes one thread decodes per step: 32 weights of one weight row.
+// Packed bytes one thread decodes per step: 16 weights (a quarter group) of one weight row.
 template <int FMT>
 struct PRaw {
-  u32x4 codes;     // INT4: 16 bytes; 2-bit formats: first 8 bytes used
+  u32x2 codes;     // INT4: 8 bytes; 2-bit formats: first 4 bytes used
   uint32_t scale;  // CCQ: scale byte; INT4 g64 / affine: bf16 bits
   uint32_t zero;
 };
@@ -71,62 +75,50 @@ __device__ __forceinline__ RowInfo row_info(const DevWeight& w, int64_t e, int64
   return r;
 }
 
-// Step `g` (group g), half `hf` (weights 32 hf .. 32 hf + 31 of the group) of one row.
+// Step `g` (group g), quarter `qt` (weights 16 qt .. 16 qt + 15 of the group) of one row.
 template <int FMT>
-__device__ __forceinline__ void pload(PRaw<FMT>& p, const RowInfo& r, int64_t g, int hf) {
+__device__ __forceinline__ void pload(PRaw<FMT>& p, const RowInfo& r, int64_t g, int qt) {
   if (FMT == FMT_INT4) {
-    p.codes = *reinterpret_cast<const u32x4*>(r.codes + g * 32 + hf * 16);
+    p.codes = *reinterpret_cast<const u32x2*>(r.codes + g * 32 + qt * 8);
     p.scale = r.scales ? (uint32_t)r.scales[g] : 0u;
   } else if (FMT == FMT_AFFINE2) {
-    const u32x2 c = *reinterpret_cast<const u32x2*>(r.codes + g * 16 + hf * 8);
-    p.codes = (u32x4){c.x, c.y, 0u, 0u};
+    p.codes.x = *reinterpret_cast<const uint32_t*>(r.codes + g * 16 + qt * 4);
     p.scale = r.scales[g];
     p.zero = r.zeros[g];
   } else {
-    const u32x2 c = *reinterpret_cast<const u32x2*>(r.codes + g * 16 + hf * 8);
-    p.codes = (u32x4){c.x, c.y, 0u, 0u};
+    p.codes.x = *reinterpret_cast<const uint32_t*>(r.codes + g * 16 + qt * 4);
     p.scale = r.qscale[g >> 1];
   }
 }
 
-// Decode 32 weights into 16 bf16 pairs (k order).
+// Decode 16 weights into 8 bf16 pairs (k order).
 template <int FMT>
 __device__ __forceinline__ void pdecode(const PRaw<FMT>& p, const RowInfo& r, int64_t g,
-                                        float zpf, uint32_t (&o)[16]) {
-  uint32_t a[8], b[8];
+                                        float zpf, uint32_t (&o)[8]) {
   if (FMT == FMT_INT4) {
     const float s = r.scales ? bf16_bits_to_f32(p.scale & 0xFFFFu) : r.fin;
-    int4_decode16(p.codes.x, p.codes.y, s, a);
-    int4_decode16(p.codes.z, p.codes.w, s, b);
+    int4_decode16(p.codes.x, p.codes.y, s, o);
   } else if (FMT == FMT_AFFINE2) {
     const float s = bf16_bits_to_f32(p.scale & 0xFFFFu);
-    const float mzs = -(float)(p.zero & 0xFFu) * s;
-    affine2_decode16(p.codes.x, s, mzs, a);
-    affine2_decode16(p.codes.y, s, mzs, b);
+    affine2_decode16(p.codes.x, s, -(float)(p.zero & 0xFFu) * s, o);
   } else {
     const float s = (float)((p.scale >> (4 * (g & 1))) & 0xFu) * r.fin;
-    ccq_decode16(p.codes.x, r.cs, r.cz, s, -zpf * s, a);
-    ccq_decode16(p.codes.y, r.cs, r.cz, s, -zpf * s, b);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    o[i] = a[i];
-    o[8 + i] = b[i];
+    ccq_decode16(p.codes.x, r.cs, r.cz, s, -zpf * s, o);
   }
 }
 
 template <int FMT, int MODE>
-__global__ __launch_bounds__(256) void tiled_kernel(const TiledArgs args) {
+__global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  // buffers: A tiles at lds + buf * TILE_BYTES, decoded weight tiles after them
-  auto As = [&](int buf) { return lds + buf * TILE_BYTES; };
-  auto Bs = [&](int buf) { return lds + (2 + buf) * TILE_BYTES; };
+  // buffers: two activation tiles, then two decoded weight tiles
+  auto As = [&](int buf) { return lds + buf * A_BYTES; };
+  auto Bs = [&](int buf) { return lds + 2 * A_BYTES + buf * B_BYTES; };
   __shared__ int32_t s_tile[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // wave quarter: rows 64 wm, columns 64 wn
+  const int wm = wave >> 1, wn = wave & 1;  // wave block: rows 64 wm (0..3), channels 64 wn
 
   // ---- which rows: dense row tile, or (expert, row tile) from the expert offsets ----
   int64_t e = 0, row0, rows;
@@ -168,8 +160,8 @@ __global__ __launch_bounds__(256) void tiled_kernel(const TiledArgs args) {
   // n0 + i, else up row n0 + i - 64 (n0 = 64 * blockIdx.x).
   const int64_t n0 = (MODE == MODE_GATEUP) ? (int64_t)blockIdx.x * 64 : (int64_t)blockIdx.x * BN;
 
-  // decode role: thread -> (tile row dr, half hf)
-  const int dr = tid >> 1, hf = tid & 1;
+  // decode role: thread -> (weight tile row dr, quarter qt of the group)
+  const int dr = tid >> 2, qt = tid & 3;
   int64_t wrow;
   const DevWeight* wsrc;
   if constexpr (MODE == MODE_GATEUP) {
@@ -185,6 +177,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const TiledArgs args) {
 
   // activation copy role: thread -> (tile row ar, half ah): 64 bytes
   const int ar = tid >> 1, ah = tid & 1;
+  const bool wave_active = 64 * wm < rows;  // some of this wave's rows are real
   const uint16_t* arow = nullptr;
   if (ar < rows) {
     const int64_t r = row0 + ar;
@@ -194,28 +187,31 @@ __global__ __launch_bounds__(256) void tiled_kernel(const TiledArgs args) {
       arow = args.a + r * args.a_stride;
   }
 
-  PRaw<FMT> pr;
-  u32x4 xa[4];
-  auto load_step = [&](int64_t g) {
-    pload<FMT>(pr, ri, g, hf);
+  // One step's global data held in registers between its load and its LDS store.
+  struct Stage {
+    PRaw<FMT> pr;
+    u32x4 xa[4];
+  };
+  auto load_step = [&](Stage& st, int64_t g) {
+    pload<FMT>(st.pr, ri, g, qt);
     if (arow) {
       const u32x4* src = reinterpret_cast<const u32x4*>(arow + g * BK + ah * 32);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xa[i] = src[i];
+      for (int i = 0; i < 4; ++i) st.xa[i] = src[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xa[i] = (u32x4){0u, 0u, 0u, 0u};
+      for (int i = 0; i < 4; ++i) st.xa[i] = (u32x4){0u, 0u, 0u, 0u};
     }
   };
-  auto store_step = [&](int64_t g, int buf) {
-    uint32_t o[16];
-    pdecode<FMT>(pr, ri, g, zpf, o);
-    u32x4* bd = reinterpret_cast<u32x4*>(Bs(buf) + dr * LPITCH + hf * 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bd[i] = (u32x4){o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+  auto store_step = [&](const Stage& st, int64_t g, int buf) {
+    uint32_t o[8];
+    pdecode<FMT>(st.pr, ri, g, zpf, o);
+    u32x4* bd = reinterpret_cast<u32x4*>(Bs(buf) + dr * LPITCH + qt * 32);
+    bd[0] = (u32x4){o[0], o[1], o[2], o[3]};
+    bd[1] = (u32x4){o[4], o[5], o[6], o[7]};
     u32x4* ad = reinterpret_cast<u32x4*>(As(buf) + ar * LPITCH + ah * 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ad[i] = xa[i];
+    for (int i = 0; i < 4; ++i) ad[i] = st.xa[i];
   };
 
   f32x16 acc[2][2];
@@ -237,29 +233,43 @@ __global__ __launch_bounds__(256) void tiled_kernel(const TiledArgs args) {
   for (int j = 0; j < 2; ++j)
     brow_l[j] = (MODE == MODE_GATEUP) ? (64 * j + 32 * wn + l32) : (64 * wn + 32 * j + l32);
 
-  load_step(0);
-  store_step(0, 0);
-  __syncthreads();
-  for (int64_t g = 0; g < steps; ++g) {
-    const int buf = (int)(g & 1);
-    const bool more = g + 1 < steps;
-    if (more) load_step(g + 1);
+  auto mfma_step = [&](int buf) {
+    if (!wave_active) return;
+    u32x4 A[BK / 16][2], B[BK / 16][2];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 A[2], B[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        A[i] = *reinterpret_cast<const u32x4*>(As(buf) + arow_l[i] * LPITCH + (ks * 16 + kh * 8) * 2);
+        A[ks][i] = *reinterpret_cast<const u32x4*>(As(buf) + arow_l[i] * LPITCH + (ks * 16 + kh * 8) * 2);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        B[j] = *reinterpret_cast<const u32x4*>(Bs(buf) + brow_l[j] * LPITCH + (ks * 16 + kh * 8) * 2);
+        B[ks][j] = *reinterpret_cast<const u32x4*>(Bs(buf) + brow_l[j] * LPITCH + (ks * 16 + kh * 8) * 2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(A[i], B[j], acc[i][j]);
-    }
-    if (more) store_step(g + 1, buf ^ 1);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(A[ks][i], B[ks][j], acc[i][j]);
+  };
+
+  // Pipeline: while step g is multiplied from LDS buffer g & 1, step g + 1 (loaded one
+  // iteration earlier) is decoded into the other buffer and step g + 2 is being loaded.
+  Stage s0, s1;
+  load_step(s0, 0);
+  if (steps > 1) load_step(s1, 1);
+  store_step(s0, 0, 0);
+  __syncthreads();
+  auto iter = [&](Stage& nxt, Stage& fut, int64_t g) {
+    const int buf = (int)(g & 1);
+    if (g + 2 < steps) load_step(fut, g + 2);  // `fut` was stored to LDS last iteration
+    mfma_step(buf);
+    if (g + 1 < steps) store_step(nxt, g + 1, buf ^ 1);
     __syncthreads();
+  };
+  for (int64_t g = 0; g < steps; g += 2) {
+    iter(s1, s0, g);
+    if (g + 1 < steps) iter(s0, s1, g + 1);
   }
 
   // ---- epilogue: lane holds D[8 (r/4) + 4 kh + r % 4][l32] of each 32 x 32 tile ----
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const TiledArgs args) {
 
 template <int FMT, int MODE>
 hipError_t launch_t(const TiledArgs& a, int64_t row_tiles, hipStream_t s) {
-  constexpr size_t lds_bytes = 4 * (size_t)TILE_BYTES;
+  constexpr size_t lds_bytes = 2 * (size_t)(A_BYTES + B_BYTES);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tiled_kernel<FMT, MODE>),
@@ -305,7 +315,7 @@ hipError_t launch_t(const TiledArgs& a, int64_t row_tiles, hipStream_t s) {
   }
   const int64_t cols = (MODE == MODE_GATEUP) ? (a.N + 63) / 64 : (a.N + BN - 1) / BN;
   dim3 grid((unsigned)cols, (unsigned)row_tiles);
-  hipLaunchKernelGGL((tiled_kernel<FMT, MODE>), grid, dim3(256), lds_bytes, s, a);
+  hipLaunchKernelGGL((tiled_kernel<FMT, MODE>), grid, dim3(NTHREADS), lds_bytes, s, a);
   return hipGetLastError();
 }
 
