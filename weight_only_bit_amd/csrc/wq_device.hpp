@@ -82,73 +82,103 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 
 // ---------------------------------------------------------------------------------------------
 // Fast exact decode for the MFMA kernels.  Each helper turns the packed bytes one lane holds
-// for a 64-weight group (16 consecutive weights of one row) into 8 dwords of bf16 pairs in k
-// order, equal bit for bit to the format's x_hat:
-//   value = bf16(fl((c - z) * s))  computed as  bf16(fma(f32(c), s, -z*s))
-// which is the same single rounding of the same exact product whenever z*s is exact in fp32
-// (z a power of two -- the CCQ zero point 32 -- or z*s with few enough bits -- the 2-bit
-// affine zero point times a bf16 scale, and INT4's 8 * s).  For c == z the fma gives +0 where
-// the two-step form gives 0 * s: the same bits for s >= 0 (scales are non-negative).
+// (16 consecutive weights of one row) into 8 dwords of bf16 pairs in k order, equal bit for
+// bit to the format's x_hat:
+//   value = bf16(fl((c - z) * s))
+//
+// The arithmetic runs on v_fma_mix_f32, which reads one operand as the low or high f16 half
+// of a dword, widens it exactly and fuses it into an fp32 FMA.  A code field c (< 1024) that
+// sits alone in a 16-bit half is, read as f16, the subnormal c * 2^-24; with the scale
+// pre-multiplied by 2^24 (exact) the mixed FMA forms the exact product c * s and rounds
+//   c * s - z * s
+// once -- the single rounding of the exact (c - z) * s whenever z * s is exact in fp32 (z a
+// power of two -- the CCQ zero point 32 -- or z * s with few enough bits: the 2-bit affine
+// zero point times a bf16 scale, INT4's 8 * s).  So one instruction converts and scales a
+// weight, and 16-bit packed shifts place two codes per dword.  For c == z the result is +0
+// where the two-step form gives 0 * s: the same bits for s >= 0 (scales are non-negative).
+// Requires f16 subnormals to be kept (the default float mode) and |s| < 2^100.
 // ---------------------------------------------------------------------------------------------
 
-// CCQ: one dword = 4 clustered bytes = 16 weights.  s = f32(s_q) * super, mzs = -zp * s.
-// CLAMP = false only when ccq_row_needs_no_clamp holds for the row.
-template <bool CLAMP = true>
-__device__ __forceinline__ void ccq_decode16(uint32_t w, float cs, float cz, float s, float mzs,
-                                             uint32_t (&p)[8]) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const uint32_t R = ccq_expand_bits<CLAMP>((float)((w >> (8 * b)) & 0xFFu), cs, cz);
-    float f[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)  // bit-shift decode: shifts 9, 6, 3, 0; mask 0x3F
-      f[j] = __builtin_fmaf((float)((R >> (9 - 3 * j)) & 0x3Fu), s, mzs);
-    p[2 * b] = cvt_pk_bf16(f[0], f[1]);
-    p[2 * b + 1] = cvt_pk_bf16(f[2], f[3]);
-  }
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kTwo24 = 16777216.0f;
+
+// Both 16-bit halves of x shifted right by sh (v_pk_lshrrev_b16).
+__device__ __forceinline__ uint32_t pk_shr16(uint32_t x, uint16_t sh) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) >> (u16x2){sh, sh});
 }
 
-// a & b, opaque to the optimizer: keeps a masked dword whole so each byte is converted by
-// one v_cvt_f32_ubyteN instead of a bit-field extract plus a convert.
-__device__ __forceinline__ uint32_t and_opaque(uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+// fl(h * a + b) with h the low / high f16 half of x (v_fma_mix_f32 op_sel).
+__device__ __forceinline__ float mix_lo(uint32_t x, float a, float b) {
+  return __builtin_fmaf((float)__builtin_bit_cast(f16x2_t, x).x, a, b);
+}
+__device__ __forceinline__ float mix_hi(uint32_t x, float a, float b) {
+  return __builtin_fmaf((float)__builtin_bit_cast(f16x2_t, x).y, a, b);
+}
+
+// CCQ: one dword = 4 clustered bytes = 16 weights.  cs24 = code_scale * 2^24, s24 = s * 2^24
+// with s = f32(s_q) * super, mzs = -zp * s.  Stage 1 uses the same mixed FMA: the byte C'
+// read as a subnormal times cs24 is the exact C' * code_scale, so t = fmaf(C', code_scale,
+// code_zero) bit for bit.  CLAMP = false only when ccq_row_needs_no_clamp holds for the row.
+template <bool CLAMP = true>
+__device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, float s24,
+                                             float mzs, uint32_t (&p)[8]) {
+  const uint32_t ev = w & 0x00FF00FFu;         // bytes 0, 2
+  const uint32_t od = (w >> 8) & 0x00FF00FFu;  // bytes 1, 3
+  float t[4] = {mix_lo(ev, cs24, cz), mix_lo(od, cs24, cz), mix_hi(ev, cs24, cz),
+                mix_hi(od, cs24, cz)};
+  uint32_t R[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (CLAMP) t[b] = __builtin_amdgcn_fmed3f(t[b], 0.0f, 32767.0f);
+    R[b] = __float_as_uint(t[b] + 12582912.0f);  // bits 0..14 = C (see ccq_expand_bits)
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t P = (R[2 * h] & 0xFFFFu) | (R[2 * h + 1] << 16);  // C of bytes 2h, 2h+1
+    // bit-shift decode: 6-bit states at shifts 9, 6, 3, 0 of each half
+    const uint32_t q0 = pk_shr16(P, 9);  // C < 2^15: no bits above the field
+    const uint32_t q1 = pk_shr16(P, 6) & 0x003F003Fu;
+    const uint32_t q2 = pk_shr16(P, 3) & 0x003F003Fu;
+    const uint32_t q3 = P & 0x003F003Fu;
+    p[4 * h + 0] = cvt_pk_bf16(mix_lo(q0, s24, mzs), mix_lo(q1, s24, mzs));
+    p[4 * h + 1] = cvt_pk_bf16(mix_lo(q2, s24, mzs), mix_lo(q3, s24, mzs));
+    p[4 * h + 2] = cvt_pk_bf16(mix_hi(q0, s24, mzs), mix_hi(q1, s24, mzs));
+    p[4 * h + 3] = cvt_pk_bf16(mix_hi(q2, s24, mzs), mix_hi(q3, s24, mzs));
+  }
 }
 
 // INT4: two dwords = 16 signed nibbles (first weight in the low nibble).  XOR 8 biases a
-// two's-complement nibble q to q + 8 in 0..15, so value = fma(f32(q + 8), s, -8 s).
-__device__ __forceinline__ void int4_decode16(uint32_t w0, uint32_t w1, float s,
+// two's-complement nibble q to q + 8 in 0..15, so value = fl((q + 8) * s - 8 s);
+// s24 = s * 2^24, m8s = -8 s.
+__device__ __forceinline__ void int4_decode16(uint32_t w0, uint32_t w1, float s24, float m8s,
                                               uint32_t (&p)[8]) {
-  const float m8s = -8.0f * s;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t d = (h ? w1 : w0) ^ 0x88888888u;
-    const uint32_t ev = and_opaque(d, 0x0F0F0F0Fu);       // nibbles 0,2,4,6 -> bytes 0..3
-    const uint32_t od = and_opaque(d >> 4, 0x0F0F0F0Fu);  // nibbles 1,3,5,7
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float a = __builtin_fmaf((float)((ev >> (8 * b)) & 0xFFu), s, m8s);
-      const float c = __builtin_fmaf((float)((od >> (8 * b)) & 0xFFu), s, m8s);
-      p[4 * h + b] = cvt_pk_bf16(a, c);
-    }
+    const uint32_t d = (h ? w1 : w0) ^ 0x88888888u;  // halves: nibbles 0..3 and 4..7
+    const uint32_t q0 = d & 0x000F000Fu;
+    const uint32_t q1 = pk_shr16(d, 4) & 0x000F000Fu;
+    const uint32_t q2 = pk_shr16(d, 8) & 0x000F000Fu;
+    const uint32_t q3 = pk_shr16(d, 12);
+    p[4 * h + 0] = cvt_pk_bf16(mix_lo(q0, s24, m8s), mix_lo(q1, s24, m8s));
+    p[4 * h + 1] = cvt_pk_bf16(mix_lo(q2, s24, m8s), mix_lo(q3, s24, m8s));
+    p[4 * h + 2] = cvt_pk_bf16(mix_hi(q0, s24, m8s), mix_hi(q1, s24, m8s));
+    p[4 * h + 3] = cvt_pk_bf16(mix_hi(q2, s24, m8s), mix_hi(q3, s24, m8s));
   }
 }
 
-// 2-bit affine: one dword = 16 codes (first in the lowest two bits); value = fma(f32(q), s,
-// -z s) with z s exact (8-bit z times a bf16 scale).
-__device__ __forceinline__ void affine2_decode16(uint32_t w, float s, float mzs,
+// 2-bit affine: one dword = 16 codes (first in the lowest two bits); value = fl(q s - z s)
+// with z s exact (8-bit z times a bf16 scale); s24 = s * 2^24, mzs = -z s.
+__device__ __forceinline__ void affine2_decode16(uint32_t w, float s24, float mzs,
                                                  uint32_t (&p)[8]) {
-  uint32_t q[4];
+  uint32_t q[8];  // q[i]: codes i (low half) and 8 + i (high half)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = and_opaque(w >> (2 * i), 0x03030303u);  // byte b: code 4b + i
+  for (int i = 0; i < 7; ++i) q[i] = pk_shr16(w, (uint16_t)(2 * i)) & 0x00030003u;
+  q[7] = pk_shr16(w, 14);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    float f[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __builtin_fmaf((float)((q[i] >> (8 * b)) & 0xFFu), s, mzs);
-    p[2 * b] = cvt_pk_bf16(f[0], f[1]);
-    p[2 * b + 1] = cvt_pk_bf16(f[2], f[3]);
+  for (int j = 0; j < 4; ++j) {
+    p[j] = cvt_pk_bf16(mix_lo(q[2 * j], s24, mzs), mix_lo(q[2 * j + 1], s24, mzs));
+    p[4 + j] = cvt_pk_bf16(mix_hi(q[2 * j], s24, mzs), mix_hi(q[2 * j + 1], s24, mzs));
   }
 }
 

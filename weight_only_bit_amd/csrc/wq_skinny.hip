@@ -176,7 +176,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   const int64_t nr = nvalid ? nrow : (N - 1);
   const int32_t g_part0 = (kw * Kpp) >> 6;  // first group of this wave's K part
   const WaveW<FMT> W = wave_weight<FMT>(mat ? args.w1 : args.w0, e, nr, kb, g_part0);
-  const float zpf = (float)args.w0.zp;
+  // Decode constants in the 2^24-scaled form of the decode helpers (exact power-of-two
+  // scalings): a zero point that is a power of two keeps -zp * s exact.
+  const float cs24 = W.cs * kTwo24, fin24 = W.fin * kTwo24;
+  const float mzp24 = -(float)args.w0.zp / kTwo24;
 
   // CCQ rows whose codes can never leave [0, 2^15 - 1] skip the clamp (one instruction per
   // byte); the choice is uniform over the wave.
@@ -245,16 +248,20 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
       for (int j = 0; j < SPC; ++j) {
         if (c * KCW + j * SSK >= Kpp) break;
         const Raw<FMT>& rw = r[j];
-        float s = 1.0f, mzs = 0.0f;
+        // s24 = s * 2^24 (the decode helpers' scaled form), mzs = -z * s
+        float s24 = 0.0f, mzs = 0.0f;
         if constexpr (FMT == FMT_CCQ2) {
-          s = (float)((rw.scale >> W.qshift) & 0xFu) * W.fin;
-          mzs = -zpf * s;
+          s24 = (float)((rw.scale >> W.qshift) & 0xFu) * fin24;  // = fl(s_q * super) * 2^24
+          mzs = s24 * mzp24;
         } else if constexpr (FMT == FMT_INT4) {
-          s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
+          s24 = bf16_bits_to_f32(rw.scale & 0xFFFFu) * kTwo24;
+          mzs = s24 * (-8.0f / kTwo24);
         } else if constexpr (FMT == FMT_INT4PC) {
-          s = W.fin;
+          s24 = fin24;
+          mzs = fin24 * (-8.0f / kTwo24);
         } else {
-          s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
+          const float s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
+          s24 = s * kTwo24;
           mzs = -(float)(rw.zero & 0xFFu) * s;
         }
         // lane's A fragments: row t*16 + nl, columns kw*KCW + j*SSK + kb*WPL + 8h
@@ -264,11 +271,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
         for (int q = 0; q < WPL / 16; ++q) {
           uint32_t p[8];
           if constexpr (FMT == FMT_CCQ2) {
-            ccq_decode16<CLAMP>(rw.codes[q], W.cs, W.cz, s, mzs, p);
+            ccq_decode16<CLAMP>(rw.codes[q], cs24, W.cz, s24, mzs, p);
           } else if constexpr (is_int4(FMT)) {
-            int4_decode16(rw.codes[2 * q], rw.codes[2 * q + 1], s, p);
+            int4_decode16(rw.codes[2 * q], rw.codes[2 * q + 1], s24, mzs, p);
           } else {
-            affine2_decode16(rw.codes[q], s, mzs, p);
+            affine2_decode16(rw.codes[q], s24, mzs, p);
           }
           const u32x4 B0 = {p[0], p[1], p[2], p[3]};
           const u32x4 B1 = {p[4], p[5], p[6], p[7]};

@@ -47,20 +47,20 @@ struct RowInfo {
   const uint16_t* scales;
   const uint8_t* zeros;
   const uint8_t* qscale;
-  float cs, cz, fin;
+  float cs24, cz, fin24;  // CCQ code scale and super / INT4 per-channel scale, times 2^24
 };
 
 template <int FMT>
 __device__ __forceinline__ RowInfo row_info(const DevWeight& w, int64_t e, int64_t row) {
   RowInfo r{};
   const int64_t n = w.n, k = w.k, G = k / 64, grow = e * n + row;
-  r.fin = 1.0f;
+  r.fin24 = kTwo24;
   if (FMT == FMT_INT4) {
     r.codes = w.codes + grow * (k / 2);
     if (w.group)
       r.scales = w.scales + grow * G;
     else
-      r.fin = bf16_bits_to_f32(w.scales[grow]);
+      r.fin24 = bf16_bits_to_f32(w.scales[grow]) * kTwo24;
   } else if (FMT == FMT_AFFINE2) {
     r.codes = w.codes + grow * (k / 4);
     r.scales = w.scales + grow * G;
@@ -68,9 +68,9 @@ __device__ __forceinline__ RowInfo row_info(const DevWeight& w, int64_t e, int64
   } else {
     r.codes = w.codes + grow * (k / 4);
     r.qscale = w.qscale + grow * ((G + 1) / 2);
-    r.cs = w.code_scale[grow];
+    r.cs24 = w.code_scale[grow] * kTwo24;
     r.cz = w.code_zero[grow];
-    r.fin = w.super_scale[grow];
+    r.fin24 = w.super_scale[grow] * kTwo24;
   }
   return r;
 }
@@ -91,19 +91,19 @@ __device__ __forceinline__ void pload(PRaw<FMT>& p, const RowInfo& r, int64_t g,
   }
 }
 
-// Decode 16 weights into 8 bf16 pairs (k order).
+// Decode 16 weights into 8 bf16 pairs (k order).  mzp24 = -zp / 2^24 (CCQ).
 template <int FMT>
 __device__ __forceinline__ void pdecode(const PRaw<FMT>& p, const RowInfo& r, int64_t g,
-                                        float zpf, uint32_t (&o)[8]) {
+                                        float mzp24, uint32_t (&o)[8]) {
   if (FMT == FMT_INT4) {
-    const float s = r.scales ? bf16_bits_to_f32(p.scale & 0xFFFFu) : r.fin;
-    int4_decode16(p.codes.x, p.codes.y, s, o);
+    const float s24 = r.scales ? bf16_bits_to_f32(p.scale & 0xFFFFu) * kTwo24 : r.fin24;
+    int4_decode16(p.codes.x, p.codes.y, s24, s24 * (-8.0f / kTwo24), o);
   } else if (FMT == FMT_AFFINE2) {
     const float s = bf16_bits_to_f32(p.scale & 0xFFFFu);
-    affine2_decode16(p.codes.x, s, -(float)(p.zero & 0xFFu) * s, o);
+    affine2_decode16(p.codes.x, s * kTwo24, -(float)(p.zero & 0xFFu) * s, o);
   } else {
-    const float s = (float)((p.scale >> (4 * (g & 1))) & 0xFu) * r.fin;
-    ccq_decode16(p.codes.x, r.cs, r.cz, s, -zpf * s, o);
+    const float s24 = (float)((p.scale >> (4 * (g & 1))) & 0xFu) * r.fin24;
+    ccq_decode16(p.codes.x, r.cs24, r.cz, s24, s24 * mzp24, o);
   }
 }
 
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
   }
   const bool wvalid = wrow < N;
   const RowInfo ri = row_info<FMT>(*wsrc, e, wvalid ? wrow : N - 1);
-  const float zpf = (float)args.w0.zp;
+  const float mzp24 = -(float)args.w0.zp / kTwo24;
 
   // activation copy role: thread -> (tile row ar, half ah): 64 bytes
   const int ar = tid >> 1, ah = tid & 1;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
   };
   auto store_step = [&](const Stage& st, int64_t g, int buf) {
     uint32_t o[8];
-    pdecode<FMT>(st.pr, ri, g, zpf, o);
+    pdecode<FMT>(st.pr, ri, g, mzp24, o);
     u32x4* bd = reinterpret_cast<u32x4*>(Bs(buf) + dr * LPITCH + qt * 32);
     bd[0] = (u32x4){o[0], o[1], o[2], o[3]};
     bd[1] = (u32x4){o[4], o[5], o[6], o[7]};
