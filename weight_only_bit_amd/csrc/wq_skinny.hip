@@ -190,7 +190,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   for (int64_t ms = 0; ms < m_total; ms += ROWS) {
     const int64_t rows_here = (m_total - ms) < ROWS ? (m_total - ms) : ROWS;
 
-    // Source rows of the activation blocks this thread stages (fixed across chunks).
+    // Source rows of the activation blocks this thread stages (fixed across chunks).  Rows
+    // past rows_here read the pass's first row (their results are never stored), and columns
+    // past the K part read column 0 and are zeroed when stored: every load in the chunk loop is
+    // unconditional, so the compiler's waits before a chunk's decode count exactly the next
+    // chunk's loads and leave them in flight.
     const uint16_t* srow[BPT];
     int sblk[BPT], srowi[BPT];
 #pragma unroll
@@ -199,37 +203,43 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
       const int row = b / (KCT / 16);
       sblk[i] = b % (KCT / 16);
       srowi[i] = row;
-      srow[i] = nullptr;
-      if (row < rows_here) {
-        const int64_t r = m_base + ms + row;
-        if constexpr (MODE == MODE_GATEUP)
-          srow[i] = args.a + (int64_t)(args.sorted_pairs[r] / args.topk) * args.a_stride;
-        else
-          srow[i] = args.a + r * args.a_stride;
-      }
+      const int64_t r = m_base + ms + (row < rows_here ? row : 0);
+      if constexpr (MODE == MODE_GATEUP)
+        srow[i] = args.a + (int64_t)(args.sorted_pairs[r] / args.topk) * args.a_stride;
+      else
+        srow[i] = args.a + r * args.a_stride;
     }
+    // Per 32-byte block, the lanes whose bit 2 is set write their second 16-byte half first,
+    // so the 8 lanes of each LDS write phase cover 8 distinct 16-byte bank groups.
+    const int swp = (lane >> 2) & 1;
     u32x4 xr[BPT][2];
     auto stage_load = [&](int c) {
 #pragma unroll
       for (int i = 0; i < BPT; ++i) {
         const int part = sblk[i] / (KCW / 16);
         const int32_t kin = c * KCW + (sblk[i] % (KCW / 16)) * 16;
-        if (srow[i] != nullptr && kin < Kpp) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(srow[i] + (int64_t)part * Kpp + kin);
-          xr[i][0] = p[0];
-          xr[i][1] = p[1];
-        } else {
-          xr[i][0] = (u32x4){0, 0, 0, 0};
-          xr[i][1] = (u32x4){0, 0, 0, 0};
-        }
+        const u32x4* p =
+            reinterpret_cast<const u32x4*>(srow[i] + (int64_t)part * Kpp + (kin < Kpp ? kin : 0));
+        xr[i][0] = p[swp];
+        xr[i][1] = p[swp ^ 1];
       }
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](int c, int buf) {
+      if ((c + 1) * KCW > Kpp) {  // last chunk of a K part that ends inside it
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+          const int32_t kin = c * KCW + (sblk[i] % (KCW / 16)) * 16;
+          if (kin >= Kpp) {
+            xr[i][0] = (u32x4){0, 0, 0, 0};
+            xr[i][1] = (u32x4){0, 0, 0, 0};
+          }
+        }
+      }
 #pragma unroll
       for (int i = 0; i < BPT; ++i) {
         u32x4* d = reinterpret_cast<u32x4*>(&lds[buf][srowi[i] * PITCH + sblk[i] * 32]);
-        d[0] = xr[i][0];
-        d[1] = xr[i][1];
+        d[swp] = xr[i][0];
+        d[swp ^ 1] = xr[i][1];
       }
     };
 
@@ -238,10 +248,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
     for (int t = 0; t < MT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     Raw<FMT> rawA[SPC], rawB[SPC];
+    // Steps past the K part are loaded too (buffer loads: in range or zero) and never decoded.
     auto load_chunk = [&](Raw<FMT>(&r)[SPC], int c) {
 #pragma unroll
-      for (int j = 0; j < SPC; ++j)
-        if (c * KCW + j * SSK < Kpp) load_raw<FMT>(r[j], W, c * SPC + j);
+      for (int j = 0; j < SPC; ++j) load_raw<FMT>(r[j], W, c * SPC + j);
     };
     auto compute_chunk = [&](Raw<FMT>(&r)[SPC], int c, int buf) {
 #pragma unroll
@@ -292,24 +302,25 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
 
     load_chunk(rawA, 0);
     stage_load(0);
-    stage_store(0);
+    stage_store(0, 0);
     __syncthreads();
     auto step = [&](Raw<FMT>(&cur)[SPC], Raw<FMT>(&nxt)[SPC], int c, int buf) {
       const bool more = (c + 1) < nchunks;
+      const int cn = more ? c + 1 : c;  // past the last chunk: reload it, store nothing
       // Staging loads first: they are waited for at the end of this chunk, and vmcnt retires
       // in order, so the weight loads issued after them stay in flight into the next chunk.
-      if (more) {
-        stage_load(c + 1);
-        load_chunk(nxt, c + 1);
-      }
+      stage_load(cn);
+      load_chunk(nxt, cn);
       compute_chunk(cur, c, buf);
-      if (more) stage_store(buf ^ 1);
+      if (more) stage_store(cn, buf ^ 1);
       __syncthreads();
     };
-    for (int c = 0; c < nchunks; c += 2) {
+    int c = 0;
+    for (; c + 1 < nchunks; c += 2) {
       step(rawA, rawB, c, 0);
-      if (c + 1 < nchunks) step(rawB, rawA, c + 1, 1);
+      step(rawB, rawA, c + 1, 1);
     }
+    if (c < nchunks) step(rawA, rawB, c, 0);
 
     // Results that meet in LDS: K parts summed in order (dense) or the up tile handed to the
     // gate wave of the same tile (gate+up).
