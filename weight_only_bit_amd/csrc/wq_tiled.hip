@@ -1,129 +1,174 @@
-// wq_tiled.hip -- weight-only GEMM for many activation rows (prefill): LDS-staged exact-bf16
-// weight tiles feeding bf16 MFMA.
+// wq_tiled.hip -- weight-only GEMM for many activation rows (prefill): exact-bf16 weights
+// decoded straight into MFMA operands, activations staged in LDS by direct-to-LDS copies.
 //
-// One workgroup = 8 waves computes a 256 (activation rows) x 128 (output channels) tile; K
-// advances one 64-weight group per step.  Per step:
-//   * the packed codes of the 128 x 64 weight tile are decoded once, by all 512 threads, to
-//     the exact bf16 weights (the same bits wq_dequantize produces) and written to LDS; each
-//     decoded weight is then used by 256 activation rows -- enough reuse that the decode's
-//     VALU work (about 4.5 instructions per CCQ weight) stays below the MFMA time;
-//   * the 256 x 64 bf16 activation tile is copied to LDS (gathered rows for MoE);
-//   * each wave multiplies a 64 x 64 block with v_mfma_f32_32x32x16_bf16 (2 x 2 tiles x 4
-//     k-steps), fp32 accumulation; waves whose rows are all past the end of a ragged tile skip
-//     their MFMAs.
-// LDS is double-buffered: the next step's packed bytes and activations are loaded into
-// registers before the current MFMAs are issued, and decoded/stored after them, so the
-// decode's VALU work overlaps the matrix-core work.
-//
-// MoE gate+up: the 128 weight rows of a tile are 64 gate rows and the matching 64 up rows, so
-// each lane holds gate and up results for the same (row, channel) and applies SiLU(g) * u in
-// the epilogue.  MoE tiles are enumerated per expert (ceil(rows / 128) row tiles each); a
-// workgroup finds its expert from the expert offsets.
+// One workgroup = 4 waves (one per SIMD) computes a 256 (activation rows) x 256 (weight rows)
+// tile; K advances one 64-weight group per step.
+//   * Weights: each wave owns 64 weight rows (MoE gate+up: 32 gate rows and the matching 32 up
+//     rows).  Lane (n, h) decodes 32 consecutive weights of each of its two rows per step
+//     (k = 32 h .. 32 h + 31 of the group) to the exact bf16 values -- the same bits
+//     wq_dequantize produces -- directly into v_mfma_f32_32x32x16_bf16 B fragments.  The MFMA
+//     k-slots of slice s take k = 32 h + 8 s + i (i < 8): any fixed order of the k-sum is the
+//     same product, and this one makes every lane's weights contiguous.  Each packed code is
+//     decoded exactly once per workgroup and serves 256 activation rows, so the decode (about
+//     3.3 VALU instructions per CCQ weight) runs in the shadow of the MFMAs of the same wave.
+//   * Activations: the 256 x 64 bf16 tile of each step is copied HBM -> LDS with
+//     global_load_lds_dwordx4 (no registers, no LDS store instructions) three steps ahead
+//     into a ring of four 32 KB buffers; rows are 128 bytes with the 16-byte pieces XOR-
+//     swizzled by row (piece p of row r sits in slot p ^ (r % 8)) so the fragment reads
+//     (32 rows, one piece) are bank-conflict free.  MoE rows are gathered by token.
+//   * Each wave multiplies all 256 rows by its 64 weight rows: 8 x 2 tiles of 32 x 32, four
+//     k-slices per step, fp32 accumulation in 256 accumulation registers.  The next slice's
+//     fragments are read while the current slice's MFMAs run, and the first slice of the next
+//     step is read right after the step's barrier, under the last slice's MFMAs.
+// Waves of a ragged tile still run every MFMA (rows past the end read the tile's first row);
+// their results are not stored.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "wq_kernels.hpp"
 
 namespace wq {
 namespace {
 
-constexpr int BM = 256;            // activation rows per tile
-constexpr int BN = 128;            // weight rows (output channels) per tile
-constexpr int BK = 64;             // k per step (one group)
-constexpr int NTHREADS = 512;      // 8 waves: 4 along rows x 2 along channels
-constexpr int LPITCH = BK * 2 + 16;  // LDS row pitch in bytes (pad: conflict-free 16 B reads)
-constexpr int A_BYTES = BM * LPITCH;
-constexpr int B_BYTES = BN * LPITCH;
+constexpr int BM = 256;        // activation rows per tile
+constexpr int BN = 256;        // weight rows per tile (4 waves x 64)
+constexpr int BK = 64;         // k per step (one group)
+constexpr int NTHREADS = 256;  // 4 waves
+constexpr int NSTAGE = 4;      // activation LDS ring
+constexpr int A_STAGE = BM * BK * 2;  // 32 KB, 128-byte rows, no padding (XOR swizzle)
 
-// Packed bytes one thread decodes per step: 16 weights (a quarter group) of one weight row.
+__shared__ __attribute__((aligned(16))) uint8_t sA0[A_STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t sA1[A_STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t sA2[A_STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t sA3[A_STAGE];
+
+template <int ST>
+__device__ __forceinline__ uint8_t* a_stage() {
+  static_assert(ST >= 0 && ST < NSTAGE, "stage");
+  if constexpr (ST == 0) return sA0;
+  else if constexpr (ST == 1) return sA1;
+  else if constexpr (ST == 2) return sA2;
+  else return sA3;
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+#define WQ_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+
+// Packed bytes one lane decodes per step for one weight row: 32 weights.
 template <int FMT>
-struct PRaw {
-  u32x2 codes;     // INT4: 8 bytes; 2-bit formats: first 4 bytes used
-  uint32_t scale;  // CCQ: scale byte; INT4 g64 / affine: bf16 bits
-  uint32_t zero;
+struct Codes {
+  u32x4 c;         // 2-bit formats: c.x, c.y (8 bytes); INT4: all 16 bytes
+  uint32_t scale;  // CCQ: scale byte; INT4 / affine: bf16 bits
+  uint32_t zero;   // affine zero point
 };
 
-struct RowInfo {
-  const uint8_t* codes;  // row start
-  const uint16_t* scales;
-  const uint8_t* zeros;
-  const uint8_t* qscale;
-  float cs24, cz, fin24;  // CCQ code scale and super / INT4 per-channel scale, times 2^24
+// Where one weight row's packed data lives; the row is copied to LDS by one lane of its wave.
+struct RowSrc {
+  const uint8_t* codes;    // row start
+  const uint8_t* scale;    // INT4 / affine: scales row (bf16, byte address); CCQ: qscale row
+  const uint8_t* zeros;    // affine zero points row
+  int32_t gstep;           // bytes between groups' scales: 2 (INT4 g64, affine) or 0 (INT4
+                           // per channel); CCQ: unused (two 4-bit scales per byte)
 };
 
 template <int FMT>
-__device__ __forceinline__ RowInfo row_info(const DevWeight& w, int64_t e, int64_t row) {
-  RowInfo r{};
+__device__ __forceinline__ RowSrc row_src(const DevWeight& w, int64_t e, int64_t row) {
+  RowSrc r{};
   const int64_t n = w.n, k = w.k, G = k / 64, grow = e * n + row;
-  r.fin24 = kTwo24;
   if (FMT == FMT_INT4) {
     r.codes = w.codes + grow * (k / 2);
-    if (w.group)
-      r.scales = w.scales + grow * G;
-    else
-      r.fin24 = bf16_bits_to_f32(w.scales[grow]) * kTwo24;
+    if (w.group) {
+      r.scale = reinterpret_cast<const uint8_t*>(w.scales + grow * G);
+      r.gstep = 2;
+    } else {
+      r.scale = reinterpret_cast<const uint8_t*>(w.scales + grow);
+      r.gstep = 0;
+    }
   } else if (FMT == FMT_AFFINE2) {
     r.codes = w.codes + grow * (k / 4);
-    r.scales = w.scales + grow * G;
+    r.scale = reinterpret_cast<const uint8_t*>(w.scales + grow * G);
     r.zeros = w.zeros + grow * G;
+    r.gstep = 2;
   } else {
     r.codes = w.codes + grow * (k / 4);
-    r.qscale = w.qscale + grow * ((G + 1) / 2);
-    r.cs24 = w.code_scale[grow] * kTwo24;
-    r.cz = w.code_zero[grow];
-    r.fin24 = w.super_scale[grow] * kTwo24;
+    r.scale = w.qscale + grow * ((G + 1) / 2);
   }
   return r;
 }
 
-// Step `g` (group g), quarter `qt` (weights 16 qt .. 16 qt + 15 of the group) of one row.
-template <int FMT>
-__device__ __forceinline__ void pload(PRaw<FMT>& p, const RowInfo& r, int64_t g, int qt) {
-  if (FMT == FMT_INT4) {
-    p.codes = *reinterpret_cast<const u32x2*>(r.codes + g * 32 + qt * 8);
-    p.scale = r.scales ? (uint32_t)r.scales[g] : 0u;
-  } else if (FMT == FMT_AFFINE2) {
-    p.codes.x = *reinterpret_cast<const uint32_t*>(r.codes + g * 16 + qt * 4);
-    p.scale = r.scales[g];
-    p.zero = r.zeros[g];
-  } else {
-    p.codes.x = *reinterpret_cast<const uint32_t*>(r.codes + g * 16 + qt * 4);
-    p.scale = r.qscale[g >> 1];
-  }
-}
+// Per-row constants of the CCQ decode (code scale and super scale times 2^24, code zero).
+struct RowConst {
+  float cs24, cz, fin24;
+};
 
-// Decode 16 weights into 8 bf16 pairs (k order).  mzp24 = -zp / 2^24 (CCQ).
+// The lane's 32 weights of one row as 16 bf16 pairs (k order).  mzp24 = -zp / 2^24 (CCQ).
 template <int FMT>
-__device__ __forceinline__ void pdecode(const PRaw<FMT>& p, const RowInfo& r, int64_t g,
-                                        float mzp24, uint32_t (&o)[8]) {
+__device__ __forceinline__ void cdecode(const Codes<FMT>& p, const RowConst& r, int64_t g,
+                                        float mzp24, uint32_t (&o)[16]) {
+  uint32_t a[8], b[8];
   if (FMT == FMT_INT4) {
-    const float s24 = r.scales ? bf16_bits_to_f32(p.scale & 0xFFFFu) * kTwo24 : r.fin24;
-    int4_decode16(p.codes.x, p.codes.y, s24, s24 * (-8.0f / kTwo24), o);
+    const float s24 = bf16_bits_to_f32(p.scale & 0xFFFFu) * kTwo24;
+    const float m8s = s24 * (-8.0f / kTwo24);
+    int4_decode16(p.c.x, p.c.y, s24, m8s, a);
+    int4_decode16(p.c.z, p.c.w, s24, m8s, b);
   } else if (FMT == FMT_AFFINE2) {
     const float s = bf16_bits_to_f32(p.scale & 0xFFFFu);
-    affine2_decode16(p.codes.x, s * kTwo24, -(float)(p.zero & 0xFFu) * s, o);
+    const float s24 = s * kTwo24, mzs = -(float)(p.zero & 0xFFu) * s;
+    affine2_decode16(p.c.x, s24, mzs, a);
+    affine2_decode16(p.c.y, s24, mzs, b);
   } else {
     const float s24 = (float)((p.scale >> (4 * (g & 1))) & 0xFu) * r.fin24;
-    ccq_decode16(p.codes.x, r.cs24, r.cz, s24, s24 * mzp24, o);
+    ccq_decode16(p.c.x, r.cs24, r.cz, s24, s24 * mzp24, a);
+    ccq_decode16(p.c.y, r.cs24, r.cz, s24, s24 * mzp24, b);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    o[i] = a[i];
+    o[8 + i] = b[i];
   }
 }
 
+// Packed-data LDS ring, per wave and stage: codes (64 rows x 16 bytes, INT4: two such halves),
+// then one dword per row for the scale, then (affine) one for the zero point.
+template <int FMT>
+struct CodeRing {
+  static constexpr int CODE_BYTES = (FMT == FMT_INT4 ? 2 : 1) * 64 * 16;
+  static constexpr int WAVE_BYTES = CODE_BYTES + 256 * (FMT == FMT_AFFINE2 ? 2 : 1);
+  static constexpr int STAGE_BYTES = 4 * WAVE_BYTES;
+  static constexpr int DEPTH = (FMT == FMT_INT4) ? 2 : 4;  // stages (fits 160 KB with A)
+  static constexpr int AHEAD = DEPTH - 1 > 2 ? DEPTH - 1 : 2;  // steps between copy and decode
+  // memory instructions per step per lane: codes, scale, zero
+  static constexpr int VMEM = (FMT == FMT_INT4 ? 2 : 1) + 1 + (FMT == FMT_AFFINE2 ? 1 : 0);
+};
+
 template <int FMT, int MODE>
-__global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  // buffers: two activation tiles, then two decoded weight tiles
-  auto As = [&](int buf) { return lds + buf * A_BYTES; };
-  auto Bs = [&](int buf) { return lds + 2 * A_BYTES + buf * B_BYTES; };
-  __shared__ int32_t s_tile[4];
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void tiled_kernel(const TiledArgs args) {
+  __shared__ int32_t s_tile[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // wave block: rows 64 wm (0..3), channels 64 wn
+  const int l32 = lane & 31, kh = lane >> 5;
+
+  // ---- which tile: XCD-aware order ----
+  // Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD w % 8).  Row tile
+  // r goes to XCD r % 8, and each XCD walks all column tiles of one row tile before the next,
+  // so the workgroups running together on an XCD share their activation tile through its L2.
+  constexpr int64_t NCOLS_PER_TILE = (MODE == MODE_GATEUP) ? BN / 2 : BN;
+  const int64_t ncols = (args.N + NCOLS_PER_TILE - 1) / NCOLS_PER_TILE;
+  const int64_t wg = blockIdx.x;
+  const int64_t li = wg >> 3;
+  const int64_t rtile = (li / ncols) * 8 + (wg & 7);
+  const int64_t ctile = li % ncols;
 
   // ---- which rows: dense row tile, or (expert, row tile) from the expert offsets ----
   int64_t e = 0, row0, rows;
   if constexpr (MODE == MODE_DENSE) {
-    row0 = (int64_t)blockIdx.y * BM;
+    row0 = rtile * BM;
+    if (row0 >= args.M) return;
     rows = args.M - row0 < BM ? args.M - row0 : BM;
   } else {
     if (tid == 0) {
@@ -133,7 +178,7 @@ __global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
       for (int ex = 0; ex < args.experts; ++ex) {
         const int64_t c = args.offsets[ex + 1] - args.offsets[ex];
         const int64_t nt = (c + BM - 1) / BM;
-        if ((int64_t)blockIdx.y < acc + nt) {
+        if (rtile < acc + nt) {
           found = ex;
           before = acc;
           break;
@@ -141,7 +186,7 @@ __global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
         acc += nt;
       }
       s_tile[0] = found;
-      s_tile[1] = (int32_t)((int64_t)blockIdx.y - before);
+      s_tile[1] = (int32_t)(rtile - before);
     }
     __syncthreads();
     if (s_tile[0] < 0) return;
@@ -152,143 +197,300 @@ __global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
     rows = base + cnt - row0 < BM ? base + cnt - row0 : BM;
   }
 
-  // ---- weight rows this workgroup covers ----
   const int64_t N = args.N;
-  const int64_t K = args.K;
-  const int64_t steps = K / BK;
-  // Weight tile row i (0..127): dense/down: channel n0 + i; gate+up: i < 64 -> gate row
-  // n0 + i, else up row n0 + i - 64 (n0 = 64 * blockIdx.x).
-  const int64_t n0 = (MODE == MODE_GATEUP) ? (int64_t)blockIdx.x * 64 : (int64_t)blockIdx.x * BN;
+  const int64_t steps = args.K / BK;
+  const int64_t last = steps - 1;
+  const int64_t n0 = ctile * NCOLS_PER_TILE;
 
-  // decode role: thread -> (weight tile row dr, quarter qt of the group)
-  const int dr = tid >> 2, qt = tid & 3;
-  int64_t wrow;
-  const DevWeight* wsrc;
-  if constexpr (MODE == MODE_GATEUP) {
-    wrow = n0 + (dr & 63);
-    wsrc = (dr < 64) ? &args.w0 : &args.w1;
-  } else {
-    wrow = n0 + dr;
-    wsrc = &args.w0;
+  // ---- weight rows ----
+  // Decode: lane (l32, kh) decodes rows j = 0, 1:
+  //   dense/down: channel n0 + 64 wave + 32 j + l32
+  //   gate+up: j = 0 -> gate row n0 + 32 wave + l32, j = 1 -> the matching up row
+  // i.e. "wave row" 32 j + l32 of the wave's 64 rows.  Copy: lane l copies wave row l.
+  using Ring = CodeRing<FMT>;
+  int64_t wrow[2];
+  RowConst rc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    wrow[j] = (MODE == MODE_GATEUP) ? n0 + 32 * wave + l32 : n0 + 64 * wave + 32 * j + l32;
+    rc[j] = RowConst{0.f, 0.f, 0.f};
+    if constexpr (FMT == FMT_CCQ2) {
+      const DevWeight& w = (MODE == MODE_GATEUP && j == 1) ? args.w1 : args.w0;
+      const int64_t grow = e * w.n + (wrow[j] < N ? wrow[j] : N - 1);
+      rc[j] = RowConst{w.code_scale[grow] * kTwo24, w.code_zero[grow], w.super_scale[grow] * kTwo24};
+    }
   }
-  const bool wvalid = wrow < N;
-  const RowInfo ri = row_info<FMT>(*wsrc, e, wvalid ? wrow : N - 1);
   const float mzp24 = -(float)args.w0.zp / kTwo24;
-
-  // activation copy role: thread -> (tile row ar, half ah): 64 bytes
-  const int ar = tid >> 1, ah = tid & 1;
-  const bool wave_active = 64 * wm < rows;  // some of this wave's rows are real
-  const uint16_t* arow = nullptr;
-  if (ar < rows) {
-    const int64_t r = row0 + ar;
-    if constexpr (MODE == MODE_GATEUP)
-      arow = args.a + (int64_t)(args.sorted_pairs[r] / args.topk) * args.a_stride;
-    else
-      arow = args.a + r * args.a_stride;
+  RowSrc rs;
+  {
+    const int jj = lane >> 5;  // wave row `lane` = 32 jj + (lane % 32)
+    const int64_t r = (MODE == MODE_GATEUP) ? n0 + 32 * wave + (lane & 31)
+                                            : n0 + 64 * wave + lane;
+    const DevWeight& w = (MODE == MODE_GATEUP && jj == 1) ? args.w1 : args.w0;
+    rs = row_src<FMT>(w, e, r < N ? r : N - 1);
   }
 
-  // One step's global data held in registers between its load and its LDS store.
-  struct Stage {
-    PRaw<FMT> pr;
-    u32x4 xa[4];
+  // ---- activation copy role ----
+  // Copy instruction i of wave w fills rows 32 i + 8 w .. + 7 of a stage (1 KB: lane l lands
+  // at byte 16 l); lane l's row is 32 i + 8 w + l / 8 and its slot l % 8 receives piece
+  // (l % 8) ^ (l / 8) of that row.  Rows past the end of a ragged tile read the tile's first
+  // row; their results are never stored.
+  const uint16_t* csrc[8];
+  {
+    const int piece = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 32 * i + 8 * wave + (lane >> 3);
+      const int64_t gr = row0 + (r < rows ? r : 0);
+      const int64_t src = (MODE == MODE_GATEUP) ? (int64_t)(args.sorted_pairs[gr] / args.topk) : gr;
+      csrc[i] = args.a + src * args.a_stride + piece * 8;
+    }
+  }
+  auto copy_a = [&](int64_t g, auto stc) __attribute__((always_inline)) {
+    uint8_t* base = a_stage<decltype(stc)::value>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(csrc[i] + g * BK),
+          (__attribute__((address_space(3))) void*)(base + (32 * i + 8 * wave) * 128), 16, 0, 0);
   };
-  auto load_step = [&](Stage& st, int64_t g) {
-    pload<FMT>(st.pr, ri, g, qt);
-    if (arow) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(arow + g * BK + ah * 32);
+
+  // ---- A fragments: rows 32 i + l32 (i < 8), slice s -> piece 4 kh + s ----
+  auto read_a = [&](u32x4(&A)[8], int s, auto stc) __attribute__((always_inline)) {
+    const uint8_t* base = a_stage<decltype(stc)::value>();
+    const int p = 4 * kh + s;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.xa[i] = src[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.xa[i] = (u32x4){0u, 0u, 0u, 0u};
+    for (int i = 0; i < 8; ++i) {
+      const int m = 32 * i + l32;
+      A[i] = *reinterpret_cast<const u32x4*>(base + m * 128 + ((p ^ (m & 7)) << 4));
     }
   };
-  auto store_step = [&](const Stage& st, int64_t g, int buf) {
-    uint32_t o[8];
-    pdecode<FMT>(st.pr, ri, g, mzp24, o);
-    u32x4* bd = reinterpret_cast<u32x4*>(Bs(buf) + dr * LPITCH + qt * 32);
-    bd[0] = (u32x4){o[0], o[1], o[2], o[3]};
-    bd[1] = (u32x4){o[4], o[5], o[6], o[7]};
-    u32x4* ad = reinterpret_cast<u32x4*>(As(buf) + ar * LPITCH + ah * 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ad[i] = st.xa[i];
-  };
 
-  f32x16 acc[2][2];
+  f32x16 acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // MFMA operand rows: A row 64 wm + 32 i + (lane % 32); B row (weight tile row):
-  //   dense/down: 64 wn + 32 j + (lane % 32); gate+up: j = 0 -> gate row 32 wn + lane % 32,
-  //   j = 1 -> the matching up row 64 + 32 wn + lane % 32.
-  const int l32 = lane & 31, kh = lane >> 5;
-  int arow_l[2], brow_l[2];
+  // B fragments of one step: slice s, row j -> 4 dwords (weights 32 kh + 8 s .. + 7).
+  uint32_t Bw[2][2][16];  // [parity][j][16 dwords]
+  auto mma = [&](const u32x4(&A)[8], const uint32_t(&B)[2][16], int s) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) arow_l[i] = 64 * wm + 32 * i + l32;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    brow_l[j] = (MODE == MODE_GATEUP) ? (64 * j + 32 * wn + l32) : (64 * wn + 32 * j + l32);
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 b = {B[j][4 * s], B[j][4 * s + 1], B[j][4 * s + 2], B[j][4 * s + 3]};
+        acc[i][j] = mfma32x32x16(A[i], b, acc[i][j]);
+      }
+  };
 
-  auto mfma_step = [&](int buf) {
-    if (!wave_active) return;
-    u32x4 A[BK / 16][2], B[BK / 16][2];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        A[ks][i] = *reinterpret_cast<const u32x4*>(As(buf) + arow_l[i] * LPITCH + (ks * 16 + kh * 8) * 2);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        B[ks][j] = *reinterpret_cast<const u32x4*>(Bs(buf) + brow_l[j] * LPITCH + (ks * 16 + kh * 8) * 2);
+  // ---- packed data: copied to this wave's part of an LDS ring, Ring::AHEAD steps ahead ----
+  __shared__ __attribute__((aligned(16))) uint8_t sC0[Ring::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sC1[Ring::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sC2[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sC3[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
+  auto c_stage = [&](auto stc) __attribute__((always_inline)) {
+    constexpr int CS = decltype(stc)::value;
+    uint8_t* base = CS == 0 ? sC0 : CS == 1 ? sC1 : CS == 2 ? sC2 : sC3;
+    return base + wave * Ring::WAVE_BYTES;
+  };
+  auto copy_codes = [&](int64_t g, auto stc) __attribute__((always_inline)) {
+    uint8_t* base = c_stage(stc);
+    if constexpr (FMT == FMT_INT4) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.codes + g * 32),
+                                       (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.codes + g * 32 + 16),
+                                       (__attribute__((address_space(3))) void*)(base + 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.scale + g * rs.gstep),
+                                       (__attribute__((address_space(3))) void*)(base + Ring::CODE_BYTES), 2, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.codes + g * 16),
+                                       (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
+      if constexpr (FMT == FMT_AFFINE2) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.scale + g * 2),
+                                         (__attribute__((address_space(3))) void*)(base + Ring::CODE_BYTES), 2, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.zeros + g),
+                                         (__attribute__((address_space(3))) void*)(base + Ring::CODE_BYTES + 256), 1, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.scale + (g >> 1)),
+                                         (__attribute__((address_space(3))) void*)(base + Ring::CODE_BYTES), 1, 0, 0);
+      }
     }
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(A[ks][i], B[ks][j], acc[i][j]);
   };
+  // The lane's packed data for its rows j = 0, 1 (wave rows 32 j + l32), half kh.  These LDS
+  // reads are written out with their own wait: the copies that filled the buffer may have
+  // been issued a loop trip earlier, and for such copies the compiler's own wait would be for
+  // every outstanding memory instruction (the copies of the next steps included).  The caller
+  // waits for the copy itself (vmcnt) first.
+  auto read_codes = [&](Codes<FMT>(&cc)[2], auto stc) __attribute__((always_inline)) {
+    const uint8_t* base = c_stage(stc);
+    const uint32_t ca = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
+        base + (FMT == FMT_INT4 ? kh * 1024 + l32 * 16 : l32 * 16 + kh * 8));
+    const uint32_t sa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
+        base + Ring::CODE_BYTES + l32 * 4);
+    if constexpr (FMT == FMT_INT4) {
+      u32x4 c0, c1;
+      uint32_t s0, s1;
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:512\n\t"
+          "ds_read_b32 %2, %5\n\t"
+          "ds_read_b32 %3, %5 offset:128\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1)
+          : "v"(ca), "v"(sa)
+          : "memory");
+      cc[0].c = c0;
+      cc[1].c = c1;
+      cc[0].scale = s0;
+      cc[1].scale = s1;
+    } else if constexpr (FMT == FMT_AFFINE2) {
+      u32x2 c0, c1;
+      uint32_t s0, s1, z0, z1;
+      asm volatile(
+          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %1, %6 offset:512\n\t"
+          "ds_read_b32 %2, %7\n\t"
+          "ds_read_b32 %3, %7 offset:128\n\t"
+          "ds_read_b32 %4, %7 offset:256\n\t"
+          "ds_read_b32 %5, %7 offset:384\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1), "=v"(z0), "=v"(z1)
+          : "v"(ca), "v"(sa)
+          : "memory");
+      cc[0].c = (u32x4){c0.x, c0.y, 0u, 0u};
+      cc[1].c = (u32x4){c1.x, c1.y, 0u, 0u};
+      cc[0].scale = s0;
+      cc[1].scale = s1;
+      cc[0].zero = z0;
+      cc[1].zero = z1;
+    } else {
+      u32x2 c0, c1;
+      uint32_t s0, s1;
+      asm volatile(
+          "ds_read_b64 %0, %4\n\t"
+          "ds_read_b64 %1, %4 offset:512\n\t"
+          "ds_read_b32 %2, %5\n\t"
+          "ds_read_b32 %3, %5 offset:128\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1)
+          : "v"(ca), "v"(sa)
+          : "memory");
+      cc[0].c = (u32x4){c0.x, c0.y, 0u, 0u};
+      cc[1].c = (u32x4){c1.x, c1.y, 0u, 0u};
+      cc[0].scale = s0;
+      cc[1].scale = s1;
+    }
+  };
+  auto clamp_step = [&](int64_t g) __attribute__((always_inline)) { return g < last ? g : last; };
+  auto decode_step = [&](int64_t g, auto cstc, uint32_t(&dst)[2][16]) __attribute__((always_inline)) {
+    Codes<FMT> cc[2];
+    read_codes(cc, cstc);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) cdecode<FMT>(cc[j], rc[j], g, mzp24, dst[j]);
+  };
+  // Memory instructions issued per iteration: packed data, then the 8 activation copies.
+  constexpr int VMEM_PER_ITER = Ring::VMEM + 8;
+  constexpr int CD = Ring::DEPTH;
 
-  // Pipeline: while step g is multiplied from LDS buffer g & 1, step g + 1 (loaded one
-  // iteration earlier) is decoded into the other buffer and step g + 2 is being loaded.
-  Stage s0, s1;
-  load_step(s0, 0);
-  if (steps > 1) load_step(s1, 1);
-  store_step(s0, 0, 0);
+  // ---- prologue: steps 0..2 of the activations and 0..AHEAD-1 of the packed data in flight,
+  // step 0 decoded and visible ----
+  copy_codes(0, std::integral_constant<int, 0>{});
+  copy_a(0, std::integral_constant<int, 0>{});
+  copy_codes(clamp_step(1), std::integral_constant<int, 1 % CD>{});
+  copy_a(clamp_step(1), std::integral_constant<int, 1>{});
+  if constexpr (Ring::AHEAD > 2) copy_codes(clamp_step(2), std::integral_constant<int, 2 % CD>{});
+  copy_a(clamp_step(2), std::integral_constant<int, 2>{});
+  __builtin_amdgcn_s_waitcnt(0);  // everything issued so far
   __syncthreads();
-  auto iter = [&](Stage& nxt, Stage& fut, int64_t g) {
-    const int buf = (int)(g & 1);
-    if (g + 2 < steps) load_step(fut, g + 2);  // `fut` was stored to LDS last iteration
-    mfma_step(buf);
-    if (g + 1 < steps) store_step(nxt, g + 1, buf ^ 1);
-    __syncthreads();
+  decode_step(0, std::integral_constant<int, 0>{}, Bw[0]);
+  u32x4 X[8], Y[8];
+  read_a(X, 0, std::integral_constant<int, 0>{});
+
+  // ---- main loop: iteration g multiplies step g (LDS stage g % 4, B parity g % 2) ----
+  //   before the barrier: slices 0..2 (slice 0 was read last iteration), the next slices'
+  //   reads, and the decode of step g + 1; wait for step g + 1's copy, barrier;
+  //   after it: packed data of step g + AHEAD and activations of step g + 3, read slice 0 of
+  //   step g + 1, slice 3 of step g.
+  auto iter = [&](int64_t g, auto stc) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int PB = ST & 1;
+    // This wave's copies of step g + 1 have landed once at most the previous iteration's
+    // memory instructions are outstanding -- or, when the packed data runs only two steps
+    // ahead, its activation copies (issued after its packed data).
+    WQ_WAIT_VMCNT(Ring::AHEAD >= 3 ? VMEM_PER_ITER : 8);
+    Codes<FMT> cc[2];
+    read_codes(cc, std::integral_constant<int, (ST + 1) % CD>{});
+    read_a(Y, 1, stc);
+    mma(X, Bw[PB], 0);
+    read_a(X, 2, stc);
+    mma(Y, Bw[PB], 1);
+    read_a(Y, 3, stc);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) cdecode<FMT>(cc[j], rc[j], clamp_step(g + 1), mzp24, Bw[PB ^ 1][j]);
+    mma(X, Bw[PB], 2);
+    // 0x100 LDS read, 0x8 MFMA, 0x2 VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    copy_codes(clamp_step(g + Ring::AHEAD), std::integral_constant<int, (ST + Ring::AHEAD) % CD>{});
+    copy_a(clamp_step(g + 3), std::integral_constant<int, (ST + 3) & 3>{});
+    read_a(X, 0, std::integral_constant<int, (ST + 1) & 3>{});
+    mma(Y, Bw[PB], 3);
+    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  for (int64_t g = 0; g < steps; g += 2) {
-    iter(s1, s0, g);
-    if (g + 1 < steps) iter(s0, s1, g + 1);
+  int64_t g = 0;
+  for (; g + 3 < steps; g += 4) {
+    iter(g, std::integral_constant<int, 0>{});
+    iter(g + 1, std::integral_constant<int, 1>{});
+    iter(g + 2, std::integral_constant<int, 2>{});
+    iter(g + 3, std::integral_constant<int, 3>{});
   }
+  if (g < steps) iter(g, std::integral_constant<int, 0>{});
+  if (g + 1 < steps) iter(g + 1, std::integral_constant<int, 1>{});
+  if (g + 2 < steps) iter(g + 2, std::integral_constant<int, 2>{});
+  __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the wave exits
 
   // ---- epilogue: lane holds D[8 (r/4) + 4 kh + r % 4][l32] of each 32 x 32 tile ----
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
+      const int m = 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
       if (m >= rows) continue;
       const int64_t grow = row0 + m;
       if constexpr (MODE == MODE_GATEUP) {
-        const int64_t n = n0 + 32 * wn + l32;
+        const int64_t n = wrow[0];
         if (n >= N) continue;
         uint16_t* h = reinterpret_cast<uint16_t*>(args.out);
-        h[grow * args.out_stride + n] = (uint16_t)f32_to_bf16_bits(silu_f32(acc[i][0][r]) * acc[i][1][r]);
+        h[grow * args.out_stride + n] =
+            (uint16_t)f32_to_bf16_bits(silu_f32(acc[i][0][r]) * acc[i][1][r]);
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int64_t n = n0 + 64 * wn + 32 * j + l32;
+          const int64_t n = wrow[j];
           if (n >= N) continue;
           if constexpr (MODE == MODE_DENSE) {
             uint16_t* y = reinterpret_cast<uint16_t*>(args.out);
@@ -305,17 +507,12 @@ __global__ __launch_bounds__(NTHREADS) void tiled_kernel(const TiledArgs args) {
 
 template <int FMT, int MODE>
 hipError_t launch_t(const TiledArgs& a, int64_t row_tiles, hipStream_t s) {
-  constexpr size_t lds_bytes = 2 * (size_t)(A_BYTES + B_BYTES);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tiled_kernel<FMT, MODE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int64_t cols = (MODE == MODE_GATEUP) ? (a.N + 63) / 64 : (a.N + BN - 1) / BN;
-  dim3 grid((unsigned)cols, (unsigned)row_tiles);
-  hipLaunchKernelGGL((tiled_kernel<FMT, MODE>), grid, dim3(NTHREADS), lds_bytes, s, a);
+  constexpr int64_t per_tile = (MODE == MODE_GATEUP) ? BN / 2 : BN;
+  const int64_t cols = (a.N + per_tile - 1) / per_tile;
+  const int64_t wgs = (row_tiles + 7) / 8 * 8 * cols;  // row tiles padded to the 8 XCDs
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)wgs);
+  hipLaunchKernelGGL((tiled_kernel<FMT, MODE>), grid, dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 
