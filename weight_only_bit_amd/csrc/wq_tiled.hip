@@ -14,8 +14,12 @@
 //   * Activations: the 256 x 64 bf16 tile of each step is copied HBM -> LDS with
 //     global_load_lds_dwordx4 (no registers, no LDS store instructions) three steps ahead
 //     into a ring of four 32 KB buffers; rows are 128 bytes with the 16-byte pieces XOR-
-//     swizzled by row (piece p of row r sits in slot p ^ (r % 8)) so the fragment reads
-//     (32 rows, one piece) are bank-conflict free.  MoE rows are gathered by token.
+//     swizzled by row pair (piece p of row r sits in slot p ^ ((r / 2) % 8)).  A 128-bit LDS
+//     read serves 16 lanes per cycle from 64 banks (256 bytes), so the fragment read -- 32
+//     consecutive rows, one piece -- is conflict free when each pair of rows (one 256-byte
+//     bank line) uses its own slot: measured, this layout streams about 3x faster than a
+//     swizzle by row (r % 8), which puts rows r and r + 8 of one cycle on the same banks.
+//     MoE rows are gathered by token.
 //   * Each wave multiplies all 256 rows by its 64 weight rows: 8 x 2 tiles of 32 x 32, four
 //     k-slices per step, fp32 accumulation in 256 accumulation registers.  The next slice's
 //     fragments are read while the current slice's MFMAs run, and the first slice of the next
@@ -232,12 +236,12 @@ void tiled_kernel(const TiledArgs args) {
 
   // ---- activation copy role ----
   // Copy instruction i of wave w fills rows 32 i + 8 w .. + 7 of a stage (1 KB: lane l lands
-  // at byte 16 l); lane l's row is 32 i + 8 w + l / 8 and its slot l % 8 receives piece
-  // (l % 8) ^ (l / 8) of that row.  Rows past the end of a ragged tile read the tile's first
+  // at byte 16 l); lane l's row is r = 32 i + 8 w + l / 8 and its slot l % 8 receives piece
+  // (l % 8) ^ ((r / 2) % 8) = (l % 8) ^ ((4 w + l / 16) % 8) of that row.  Rows past the end of a ragged tile read the tile's first
   // row; their results are never stored.
   const uint16_t* csrc[8];
   {
-    const int piece = (lane & 7) ^ (lane >> 3);
+    const int piece = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 32 * i + 8 * wave + (lane >> 3);
@@ -255,14 +259,15 @@ void tiled_kernel(const TiledArgs args) {
           (__attribute__((address_space(3))) void*)(base + (32 * i + 8 * wave) * 128), 16, 0, 0);
   };
 
-  // ---- A fragments: rows 32 i + l32 (i < 8), slice s -> piece 4 kh + s ----
+  // ---- A fragments: rows m = 32 i + l32 (i < 8), slice s -> piece 4 kh + s, in slot
+  // (4 kh + s) ^ ((m / 2) % 8) = (4 kh + s) ^ ((l32 / 2) % 8) ----
   auto read_a = [&](u32x4(&A)[8], int s, auto stc) __attribute__((always_inline)) {
     const uint8_t* base = a_stage<decltype(stc)::value>();
     const int p = 4 * kh + s;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int m = 32 * i + l32;
-      A[i] = *reinterpret_cast<const u32x4*>(base + m * 128 + ((p ^ (m & 7)) << 4));
+      A[i] = *reinterpret_cast<const u32x4*>(base + m * 128 + ((p ^ ((l32 >> 1) & 7)) << 4));
     }
   };
 
