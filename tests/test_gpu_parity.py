@@ -139,6 +139,32 @@ def test_gemm_deterministic(wq):
 
 
 @pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+def test_tiled_gemm_repeatable_short_k(wq, name):
+    # Many activation rows (tiled kernel) with short K: every step of the pipeline is a
+    # prologue or tail step.  Repeated launches must give identical bits within tolerance of
+    # the oracle (a read of the packed codes that raced its own results once gave wrong
+    # 32-column blocks here, intermittently).
+    import torch
+
+    fmt = FMTS["int4" if name == "int4pc" else name]
+    group = 0 if name == "int4pc" else 64
+    for k in (64, 128, 192):
+        n, m = 320, 64
+        p = _quant(fmt, (n, k), (21, fmt, group, k), group=group)
+        x = synth.acts_bf16((m, k), 22, k)
+        ref = oracle.gemm(x, p)
+        d = to_device(p)
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        first = None
+        for rep in range(6):
+            y = torch_bf16_bits(wq.wq_gemm(xd, d))
+            assert_close(y, ref, f"tiled {name} k={k} rep {rep}")
+            if first is None:
+                first = y
+            assert np.array_equal(y, first), f"tiled {name} k={k}: run {rep} differs from run 0"
+
+
+@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
 def test_gemm_decodes_every_weight_bit_exact(wq, name):
     # Identity activations: row m of x = e_(c0+m) makes y[m][n] = W_hat[n][c0+m], one exact
     # product rounded back to the same bf16 -- so the product path's decode of every weight
@@ -164,7 +190,9 @@ def test_gemm_decodes_every_weight_bit_exact(wq, name):
 
 @pytest.mark.parametrize("t,topk,experts,kind", [(1, 8, 64, "uniform"), (7, 2, 8, "uniform"),
                                                  (300, 8, 64, "uniform"), (4096, 8, 64, "zipf"),
-                                                 (33, 4, 300, "uniform")])
+                                                 (33, 4, 300, "uniform"), (50, 1, 1, "uniform"),
+                                                 (20, 8, 512, "uniform"), (1000, 6, 16, "zipf"),
+                                                 (0, 8, 64, "uniform")])
 def test_route_exact(wq, t, topk, experts, kind):
     import torch
 

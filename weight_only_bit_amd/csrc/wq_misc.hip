@@ -61,83 +61,102 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DevWeight w, int64_t
 }
 
 // ---------------------------------------------------------------------------------------------
-// Routing: one workgroup of 1024 threads.
-//   pass 1: per-expert counts (LDS integer atomics; the totals do not depend on order);
-//   scan:   offsets = exclusive prefix sum of the counts;
-//   pass 2: 1024 pairs per round; a pair's slot is offsets[e] + (pairs of e in earlier rounds)
-//           + (pairs of e in earlier waves of this round) + (its rank among the lanes of its
-//           wave with the same expert), which keeps the pairs of an expert in increasing p.
+// Routing: a stable counting sort of the pairs by expert, in one workgroup of T threads.
+// Thread t owns the contiguous pairs [t c, (t + 1) c) (c = ceil(npairs / T)) and a private row
+// of E counters in LDS (T * E <= 32768 int32, 128 KB):
+//   pass 1: each thread counts its pairs per expert in its own row (no atomics);
+//   scan:   column sums give the expert totals, their exclusive scan the expert offsets; each
+//           counter is then replaced by offsets[e] + (pairs of e owned by threads t' < t);
+//   pass 2: each thread walks its pairs again in order and places pair p at its counter,
+//           incrementing it -- so an expert's pairs land in increasing p.
+// Ids outside [0, E) are dropped (never counted or placed), so a bad routing table cannot
+// make any kernel write out of bounds.
 // ---------------------------------------------------------------------------------------------
-constexpr int ROUTE_THREADS = 1024;
-constexpr int ROUTE_WAVES = ROUTE_THREADS / 64;
+constexpr int ROUTE_MAX_THREADS = 1024;
+constexpr int ROUTE_LDS_COUNTERS = 32768;
 
-__global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const int32_t* __restrict__ ids,
-                                                              int64_t npairs, int32_t experts,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ sorted) {
+int route_threads(int32_t experts) {
+  int t = ROUTE_LDS_COUNTERS / experts;
+  if (t > ROUTE_MAX_THREADS) t = ROUTE_MAX_THREADS;
+  int p = 64;
+  while (p * 2 <= t) p *= 2;  // a power of two, at least one wave
+  return p;
+}
+
+__global__ __launch_bounds__(ROUTE_MAX_THREADS) void route_kernel(const int32_t* __restrict__ ids,
+                                                                  int64_t npairs, int32_t experts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ sorted) {
   extern __shared__ int32_t sm[];
-  int32_t* cnt = sm;                     // [experts]
-  int32_t* run = cnt + experts;          // [experts] next free slot per expert
-  int32_t* wc = run + experts;           // [ROUTE_WAVES][experts]
+  const int T = blockDim.x;
+  const int E = experts;
+  int32_t* cnt = sm;                   // [T][E]
+  const int S = T >= E ? T / E : 1;    // scan segments per expert
+  const int R = T / S;                 // counter rows per segment
+  int32_t* part = cnt + T * E;         // [S][E] segment sums
+  int32_t* base = part + S * E;        // [E] expert offsets
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  for (int i = tid; i < experts; i += ROUTE_THREADS) cnt[i] = 0;
-  for (int i = tid; i < ROUTE_WAVES * experts; i += ROUTE_THREADS) wc[i] = 0;
+  const int64_t c = (npairs + T - 1) / T;
+  const int64_t p0 = (int64_t)tid * c;
+  const int64_t p1 = p0 + c < npairs ? p0 + c : npairs;
+
+  for (int i = tid; i < T * E; i += T) cnt[i] = 0;
   __syncthreads();
-  // Ids outside [0, experts) are dropped (never counted or placed) so a bad routing table
-  // cannot make any kernel write out of bounds.
-  for (int64_t p = tid; p < npairs; p += ROUTE_THREADS) {
+  int32_t* row = cnt + tid * E;
+  for (int64_t p = p0; p < p1; ++p) {
     const int32_t e = ids[p];
-    if (e >= 0 && e < experts) atomicAdd(&cnt[e], 1);
+    if (e >= 0 && e < E) row[e] += 1;
   }
   __syncthreads();
-  if (tid == 0) {
-    int32_t s = 0;
-    for (int e = 0; e < experts; ++e) {
-      offsets[e] = s;
-      run[e] = s;
-      s += cnt[e];
-    }
-    offsets[experts] = s;
+  // segment sums: (expert e, segment g) covers counter rows g R .. g R + R - 1
+  for (int idx = tid; idx < S * E; idx += T) {
+    const int e = idx % E, g = idx / E;
+    int32_t sum = 0;
+    for (int r = g * R; r < g * R + R; ++r) sum += cnt[r * E + e];
+    part[g * E + e] = sum;
   }
   __syncthreads();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = 0; base < npairs; base += ROUTE_THREADS) {
-    const int64_t p = base + tid;
-    int32_t e = (p < npairs) ? ids[p] : -1;
-    if (e >= experts) e = -1;
-    bool done = e < 0;
-    int32_t rank = 0;
-    // Peel off one expert value at a time, led by the lowest pending lane.
-    while (true) {
-      const uint64_t pending = __ballot(!done);
-      if (pending == 0) break;
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int32_t el = __shfl(e, leader);
-      const bool mine = !done && e == el;
-      const uint64_t m = __ballot(mine);
-      if (mine) {
-        rank = __popcll(m & lt_mask);
-        done = true;
-      }
-      if (lane == leader) wc[wave * experts + el] = __popcll(m);
+  // expert totals and their exclusive scan (wave 0; lane l takes a block of experts)
+  if (tid < 64) {
+    const int per = (E + 63) / 64;
+    const int e0 = tid * per;
+    int32_t local = 0;
+    for (int e = e0; e < e0 + per && e < E; ++e) {
+      int32_t tot = 0;
+      for (int g = 0; g < S; ++g) tot += part[g * E + e];
+      base[e] = tot;
+      local += tot;
     }
-    __syncthreads();
-    for (int ex = tid; ex < experts; ex += ROUTE_THREADS) {
-      int32_t r = run[ex];
-      for (int w = 0; w < ROUTE_WAVES; ++w) {
-        const int32_t c = wc[w * experts + ex];
-        wc[w * experts + ex] = r;
-        r += c;
-      }
-      run[ex] = r;
+    int32_t incl = local;  // inclusive scan of the lane sums
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t v = __shfl_up(incl, d);
+      if (tid >= d) incl += v;
     }
-    __syncthreads();
-    if (e >= 0) sorted[wc[wave * experts + e] + rank] = (int32_t)p;
-    __syncthreads();
-    for (int i = tid; i < ROUTE_WAVES * experts; i += ROUTE_THREADS) wc[i] = 0;
-    __syncthreads();
+    int32_t run = incl - local;
+    for (int e = e0; e < e0 + per && e < E; ++e) {
+      const int32_t tot = base[e];
+      base[e] = run;
+      offsets[e] = run;
+      run += tot;
+    }
+    if (tid == 63) offsets[E] = incl;
+  }
+  __syncthreads();
+  // counters -> first slot of each (thread, expert)
+  for (int idx = tid; idx < S * E; idx += T) {
+    const int e = idx % E, g = idx / E;
+    int32_t run = base[e];
+    for (int gg = 0; gg < g; ++gg) run += part[gg * E + e];
+    for (int r = g * R; r < g * R + R; ++r) {
+      const int32_t v = cnt[r * E + e];
+      cnt[r * E + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  for (int64_t p = p0; p < p1; ++p) {
+    const int32_t e = ids[p];
+    if (e >= 0 && e < E) sorted[row[e]++] = (int32_t)p;
   }
 }
 
@@ -185,9 +204,20 @@ hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t
 
 hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int32_t* offsets,
                         int32_t* sorted_pairs, hipStream_t stream) {
-  const size_t lds = sizeof(int32_t) * (size_t)experts * (2 + ROUTE_WAVES);
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(ROUTE_THREADS), lds, stream, ids, npairs,
-                     experts, offsets, sorted_pairs);
+  if (experts <= 0 || experts > ROUTE_LDS_COUNTERS / 64) return hipErrorInvalidValue;
+  const int T = route_threads(experts);
+  const int S = T >= experts ? T / experts : 1;
+  const size_t lds = sizeof(int32_t) * ((size_t)T * experts + (size_t)S * experts + experts);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(sizeof(int32_t) * (ROUTE_LDS_COUNTERS + 2 * 1024 + 512)));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(T), lds, stream, ids, npairs, experts, offsets,
+                     sorted_pairs);
   return hipGetLastError();
 }
 

@@ -328,7 +328,9 @@ void tiled_kernel(const TiledArgs args) {
   // reads are written out with their own wait: the copies that filled the buffer may have
   // been issued a loop trip earlier, and for such copies the compiler's own wait would be for
   // every outstanding memory instruction (the copies of the next steps included).  The caller
-  // waits for the copy itself (vmcnt) first.
+  // waits for the copy itself (vmcnt) first.  The outputs are early-clobber: a read's result
+  // may land while a later read of the block has not yet issued, so no result register may
+  // share a register with an address.
   auto read_codes = [&](Codes<FMT>(&cc)[2], auto stc) __attribute__((always_inline)) {
     const uint8_t* base = c_stage(stc);
     const uint32_t ca = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
@@ -344,7 +346,7 @@ void tiled_kernel(const TiledArgs args) {
           "ds_read_b32 %2, %5\n\t"
           "ds_read_b32 %3, %5 offset:128\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1)
+          : "=&v"(c0), "=&v"(c1), "=&v"(s0), "=&v"(s1)
           : "v"(ca), "v"(sa)
           : "memory");
       cc[0].c = c0;
@@ -362,7 +364,7 @@ void tiled_kernel(const TiledArgs args) {
           "ds_read_b32 %4, %7 offset:256\n\t"
           "ds_read_b32 %5, %7 offset:384\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1), "=v"(z0), "=v"(z1)
+          : "=&v"(c0), "=&v"(c1), "=&v"(s0), "=&v"(s1), "=&v"(z0), "=&v"(z1)
           : "v"(ca), "v"(sa)
           : "memory");
       cc[0].c = (u32x4){c0.x, c0.y, 0u, 0u};
@@ -380,7 +382,7 @@ void tiled_kernel(const TiledArgs args) {
           "ds_read_b32 %2, %5\n\t"
           "ds_read_b32 %3, %5 offset:128\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(c0), "=v"(c1), "=v"(s0), "=v"(s1)
+          : "=&v"(c0), "=&v"(c1), "=&v"(s0), "=&v"(s1)
           : "v"(ca), "v"(sa)
           : "memory");
       cc[0].c = (u32x4){c0.x, c0.y, 0u, 0u};
