@@ -111,7 +111,7 @@ DENSE_SHAPES = [(80, 576), (128, 1024), (512, 512)]
 
 @pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
 @pytest.mark.parametrize("nk", DENSE_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
-@pytest.mark.parametrize("m", [1, 3, 16, 17, 32, 33, 70])
+@pytest.mark.parametrize("m", [1, 3, 16, 17, 32, 33, 70, 150, 276])
 def test_gemm_parity(wq, name, nk, m):
     import torch
 

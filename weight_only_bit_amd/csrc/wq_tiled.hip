@@ -35,7 +35,7 @@
 namespace wq {
 namespace {
 
-constexpr int BM = 256;        // activation rows per tile
+constexpr int BM = 256;        // activation rows per full tile (8 MFMA row blocks of 32)
 constexpr int BN = 256;        // weight rows per tile (4 waves x 64)
 constexpr int BK = 64;         // k per step (one group)
 constexpr int NTHREADS = 256;  // 4 waves
@@ -147,59 +147,37 @@ struct CodeRing {
   static constexpr int VMEM = (FMT == FMT_INT4 ? 2 : 1) + 1 + (FMT == FMT_AFFINE2 ? 1 : 0);
 };
 
-template <int FMT, int MODE>
-__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void tiled_kernel(const TiledArgs args) {
-  __shared__ int32_t s_tile[2];
+// Row tiles.  An expert's (or the dense matrix's) rows are covered by full 256-row tiles; the
+// remainder rem = rows % 256 goes to one tile of the smallest of 256, 128, 64 or 32 rows that
+// holds it.  Kernel instances are per tile size (MT = rows / 32 MFMA row blocks): a launch
+// with MT = 8 covers the full tiles and remainders above 128, the others one remainder each.
+__host__ __device__ constexpr int tail_mt(int64_t rem) {
+  return rem > 128 ? 8 : rem > 64 ? 4 : rem > 32 ? 2 : 1;
+}
+// Tiles of size class MT among `count` rows, and the first row of tile i of that class.
+__device__ __forceinline__ int64_t class_tiles(int MT, int64_t count) {
+  const int64_t rem = count % BM;
+  if (MT == 8) return count / BM + (rem > 128 ? 1 : 0);
+  return (rem > 0 && tail_mt(rem) == MT) ? 1 : 0;
+}
+__device__ __forceinline__ int64_t class_row0(int MT, int64_t count, int64_t i) {
+  return MT == 8 ? i * BM : (count / BM) * BM;
+}
 
+// Per-format LDS ring of packed data (declared by the kernel, shared by its tile sizes).
+struct CodeStages {
+  uint8_t* s[4];
+};
+
+// One tile: rows row0 .. row0 + rows - 1 (at most 32 MT) of expert e, weight-row tile ctile.
+template <int FMT, int MODE, int MT>
+__device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStages& cs, int64_t e,
+                                          int64_t row0, int64_t rows, int64_t ctile) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31, kh = lane >> 5;
-
-  // ---- which tile: XCD-aware order ----
-  // Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD w % 8).  Row tile
-  // r goes to XCD r % 8, and each XCD walks all column tiles of one row tile before the next,
-  // so the workgroups running together on an XCD share their activation tile through its L2.
   constexpr int64_t NCOLS_PER_TILE = (MODE == MODE_GATEUP) ? BN / 2 : BN;
-  const int64_t ncols = (args.N + NCOLS_PER_TILE - 1) / NCOLS_PER_TILE;
-  const int64_t wg = blockIdx.x;
-  const int64_t li = wg >> 3;
-  const int64_t rtile = (li / ncols) * 8 + (wg & 7);
-  const int64_t ctile = li % ncols;
-
-  // ---- which rows: dense row tile, or (expert, row tile) from the expert offsets ----
-  int64_t e = 0, row0, rows;
-  if constexpr (MODE == MODE_DENSE) {
-    row0 = rtile * BM;
-    if (row0 >= args.M) return;
-    rows = args.M - row0 < BM ? args.M - row0 : BM;
-  } else {
-    if (tid == 0) {
-      int64_t acc = 0;
-      int found = -1;
-      int64_t before = 0;
-      for (int ex = 0; ex < args.experts; ++ex) {
-        const int64_t c = args.offsets[ex + 1] - args.offsets[ex];
-        const int64_t nt = (c + BM - 1) / BM;
-        if (rtile < acc + nt) {
-          found = ex;
-          before = acc;
-          break;
-        }
-        acc += nt;
-      }
-      s_tile[0] = found;
-      s_tile[1] = (int32_t)(rtile - before);
-    }
-    __syncthreads();
-    if (s_tile[0] < 0) return;
-    e = s_tile[0];
-    const int64_t base = args.offsets[e];
-    const int64_t cnt = args.offsets[e + 1] - base;
-    row0 = base + (int64_t)s_tile[1] * BM;
-    rows = base + cnt - row0 < BM ? base + cnt - row0 : BM;
-  }
 
   const int64_t N = args.N;
   const int64_t steps = args.K / BK;
@@ -239,11 +217,11 @@ void tiled_kernel(const TiledArgs args) {
   // at byte 16 l); lane l's row is r = 32 i + 8 w + l / 8 and its slot l % 8 receives piece
   // (l % 8) ^ ((r / 2) % 8) = (l % 8) ^ ((4 w + l / 16) % 8) of that row.  Rows past the end of a ragged tile read the tile's first
   // row; their results are never stored.
-  const uint16_t* csrc[8];
+  const uint16_t* csrc[MT];
   {
     const int piece = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MT; ++i) {
       const int r = 32 * i + 8 * wave + (lane >> 3);
       const int64_t gr = row0 + (r < rows ? r : 0);
       const int64_t src = (MODE == MODE_GATEUP) ? (int64_t)(args.sorted_pairs[gr] / args.topk) : gr;
@@ -253,7 +231,7 @@ void tiled_kernel(const TiledArgs args) {
   auto copy_a = [&](int64_t g, auto stc) __attribute__((always_inline)) {
     uint8_t* base = a_stage<decltype(stc)::value>();
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MT; ++i)
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(csrc[i] + g * BK),
           (__attribute__((address_space(3))) void*)(base + (32 * i + 8 * wave) * 128), 16, 0, 0);
@@ -261,19 +239,19 @@ void tiled_kernel(const TiledArgs args) {
 
   // ---- A fragments: rows m = 32 i + l32 (i < 8), slice s -> piece 4 kh + s, in slot
   // (4 kh + s) ^ ((m / 2) % 8) = (4 kh + s) ^ ((l32 / 2) % 8) ----
-  auto read_a = [&](u32x4(&A)[8], int s, auto stc) __attribute__((always_inline)) {
+  auto read_a = [&](u32x4(&A)[MT], int s, auto stc) __attribute__((always_inline)) {
     const uint8_t* base = a_stage<decltype(stc)::value>();
     const int p = 4 * kh + s;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MT; ++i) {
       const int m = 32 * i + l32;
       A[i] = *reinterpret_cast<const u32x4*>(base + m * 128 + ((p ^ ((l32 >> 1) & 7)) << 4));
     }
   };
 
-  f32x16 acc[8][2];
+  f32x16 acc[MT][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -281,9 +259,9 @@ void tiled_kernel(const TiledArgs args) {
 
   // B fragments of one step: slice s, row j -> 4 dwords (weights 32 kh + 8 s .. + 7).
   uint32_t Bw[2][2][16];  // [parity][j][16 dwords]
-  auto mma = [&](const u32x4(&A)[8], const uint32_t(&B)[2][16], int s) __attribute__((always_inline)) {
+  auto mma = [&](const u32x4(&A)[MT], const uint32_t(&B)[2][16], int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const u32x4 b = {B[j][4 * s], B[j][4 * s + 1], B[j][4 * s + 2], B[j][4 * s + 3]};
@@ -292,14 +270,9 @@ void tiled_kernel(const TiledArgs args) {
   };
 
   // ---- packed data: copied to this wave's part of an LDS ring, Ring::AHEAD steps ahead ----
-  __shared__ __attribute__((aligned(16))) uint8_t sC0[Ring::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sC1[Ring::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sC2[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sC3[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
   auto c_stage = [&](auto stc) __attribute__((always_inline)) {
     constexpr int CS = decltype(stc)::value;
-    uint8_t* base = CS == 0 ? sC0 : CS == 1 ? sC1 : CS == 2 ? sC2 : sC3;
-    return base + wave * Ring::WAVE_BYTES;
+    return cs.s[CS] + wave * Ring::WAVE_BYTES;
   };
   auto copy_codes = [&](int64_t g, auto stc) __attribute__((always_inline)) {
     uint8_t* base = c_stage(stc);
@@ -399,7 +372,7 @@ void tiled_kernel(const TiledArgs args) {
     for (int j = 0; j < 2; ++j) cdecode<FMT>(cc[j], rc[j], g, mzp24, dst[j]);
   };
   // Memory instructions issued per iteration: packed data, then the 8 activation copies.
-  constexpr int VMEM_PER_ITER = Ring::VMEM + 8;
+  constexpr int VMEM_PER_ITER = Ring::VMEM + MT;
   constexpr int CD = Ring::DEPTH;
 
   // ---- prologue: steps 0..2 of the activations and 0..AHEAD-1 of the packed data in flight,
@@ -413,7 +386,7 @@ void tiled_kernel(const TiledArgs args) {
   __builtin_amdgcn_s_waitcnt(0);  // everything issued so far
   __syncthreads();
   decode_step(0, std::integral_constant<int, 0>{}, Bw[0]);
-  u32x4 X[8], Y[8];
+  u32x4 X[MT], Y[MT];
   read_a(X, 0, std::integral_constant<int, 0>{});
 
   // ---- main loop: iteration g multiplies step g (LDS stage g % 4, B parity g % 2) ----
@@ -427,7 +400,7 @@ void tiled_kernel(const TiledArgs args) {
     // This wave's copies of step g + 1 have landed once at most the previous iteration's
     // memory instructions are outstanding -- or, when the packed data runs only two steps
     // ahead, its activation copies (issued after its packed data).
-    WQ_WAIT_VMCNT(Ring::AHEAD >= 3 ? VMEM_PER_ITER : 8);
+    WQ_WAIT_VMCNT(Ring::AHEAD >= 3 ? VMEM_PER_ITER : MT);
     Codes<FMT> cc[2];
     read_codes(cc, std::integral_constant<int, (ST + 1) % CD>{});
     read_a(Y, 1, stc);
@@ -439,23 +412,23 @@ void tiled_kernel(const TiledArgs args) {
     for (int j = 0; j < 2; ++j) cdecode<FMT>(cc[j], rc[j], clamp_step(g + 1), mzp24, Bw[PB ^ 1][j]);
     mma(X, Bw[PB], 2);
     // 0x100 LDS read, 0x8 MFMA, 0x2 VALU
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 2 * MT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 2 * MT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 2 * MT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -464,8 +437,8 @@ void tiled_kernel(const TiledArgs args) {
     read_a(X, 0, std::integral_constant<int, (ST + 1) & 3>{});
     mma(Y, Bw[PB], 3);
     __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM reads
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MT, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   int64_t g = 0;
@@ -482,7 +455,7 @@ void tiled_kernel(const TiledArgs args) {
 
   // ---- epilogue: lane holds D[8 (r/4) + 4 kh + r % 4][l32] of each 32 x 32 tile ----
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
@@ -513,10 +486,103 @@ void tiled_kernel(const TiledArgs args) {
 }
 
 template <int FMT, int MODE>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void tiled_kernel(const TiledArgs args) {
+  using Ring = CodeRing<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t sC0[Ring::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sC1[Ring::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t sC2[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sC3[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
+  __shared__ int32_t s_tile[3];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+
+  // ---- which tile: XCD-aware order ----
+  // Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD w % 8).  Row tile
+  // r goes to XCD r % 8, and each XCD walks all column tiles of one row tile before the next,
+  // so the workgroups running together on an XCD share their activation tile through its L2.
+  constexpr int64_t NCOLS_PER_TILE = (MODE == MODE_GATEUP) ? BN / 2 : BN;
+  const int64_t ncols = (args.N + NCOLS_PER_TILE - 1) / NCOLS_PER_TILE;
+  const int64_t wg = blockIdx.x;
+  const int64_t li = wg >> 3;
+  const int64_t rtile = (li / ncols) * 8 + (wg & 7);
+  const int64_t ctile = li % ncols;
+
+  // ---- the row tile: index rtile in the list [tiles of 256 rows][remainders of 128][64][32]
+  // (each class in expert order), then its expert and rows ----
+  int mt;
+  int64_t e = 0, row0, rows;
+  if constexpr (MODE == MODE_DENSE) {
+    const int64_t nfull = class_tiles(8, args.M), rem = args.M % BM;
+    if (rtile < nfull) {
+      mt = 8;
+      row0 = rtile * BM;
+    } else {
+      if (rtile > nfull || rem == 0 || rem > 128) return;
+      mt = tail_mt(rem);
+      row0 = (args.M / BM) * BM;
+    }
+    rows = args.M - row0 < BM ? args.M - row0 : BM;
+  } else {
+    if (tid < 64) {  // wave 0: per-expert tile counts, scanned 64 experts at a time
+      int64_t idx = rtile;
+      int found_e = -1, found_c = 0, local = 0;
+      for (int ci = 0; ci < 4 && found_e < 0; ++ci) {
+        const int cls = 8 >> ci;
+        for (int eb = 0; eb < args.experts && found_e < 0; eb += 64) {
+          const int ex = eb + lane;
+          int32_t nt = 0;
+          if (ex < args.experts) nt = (int32_t)class_tiles(cls, args.offsets[ex + 1] - args.offsets[ex]);
+          int32_t incl = nt;
+          for (int d = 1; d < 64; d <<= 1) {
+            const int32_t v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+          }
+          const int32_t total = __shfl(incl, 63);
+          if (idx < total) {
+            const uint64_t m = __ballot(idx >= incl - nt && idx < incl);
+            const int src = __ffsll((unsigned long long)m) - 1;
+            found_e = eb + src;
+            found_c = cls;
+            local = (int)(idx - __shfl(incl - nt, src));
+          } else {
+            idx -= total;
+          }
+        }
+      }
+      if (lane == 0) {
+        s_tile[0] = found_e;
+        s_tile[1] = found_c;
+        s_tile[2] = local;
+      }
+    }
+    __syncthreads();
+    if (s_tile[0] < 0) return;
+    e = s_tile[0];
+    mt = s_tile[1];
+    const int64_t base = args.offsets[e];
+    const int64_t cnt = args.offsets[e + 1] - base;
+    row0 = base + class_row0(mt, cnt, s_tile[2]);
+    rows = base + cnt - row0 < BM ? base + cnt - row0 : BM;
+  }
+  const CodeStages cs{{sC0, sC1, sC2, sC3}};
+  switch (mt) {
+    case 8: tile_body<FMT, MODE, 8>(args, cs, e, row0, rows, ctile); break;
+    case 4: tile_body<FMT, MODE, 4>(args, cs, e, row0, rows < 128 ? rows : 128, ctile); break;
+    case 2: tile_body<FMT, MODE, 2>(args, cs, e, row0, rows < 64 ? rows : 64, ctile); break;
+    default: tile_body<FMT, MODE, 1>(args, cs, e, row0, rows < 32 ? rows : 32, ctile); break;
+  }
+}
+
+// One launch: the tile list holds the full tiles and every remainder tile (MoE: row_tiles
+// bounds the 256-row tiles; each expert adds at most one smaller remainder tile).
+template <int FMT, int MODE>
 hipError_t launch_t(const TiledArgs& a, int64_t row_tiles, hipStream_t s) {
+  const int64_t tiles = (MODE == MODE_DENSE) ? a.M / BM + 1 : row_tiles + a.experts;
+  if (tiles <= 0) return hipSuccess;
   constexpr int64_t per_tile = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   const int64_t cols = (a.N + per_tile - 1) / per_tile;
-  const int64_t wgs = (row_tiles + 7) / 8 * 8 * cols;  // row tiles padded to the 8 XCDs
+  const int64_t wgs = (tiles + 7) / 8 * 8 * cols;  // row tiles padded to the 8 XCDs
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
   hipLaunchKernelGGL((tiled_kernel<FMT, MODE>), grid, dim3(NTHREADS), 0, s, a);
