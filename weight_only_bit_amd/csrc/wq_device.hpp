@@ -127,15 +127,19 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, f
   const uint32_t od = (w >> 8) & 0x00FF00FFu;  // bytes 1, 3
   float t[4] = {mix_lo(ev, cs24, cz), mix_lo(od, cs24, cz), mix_hi(ev, cs24, cz),
                 mix_hi(od, cs24, cz)};
-  uint32_t R[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < 4; ++b)
     if (CLAMP) t[b] = __builtin_amdgcn_fmed3f(t[b], 0.0f, 32767.0f);
-    R[b] = __float_as_uint(t[b] + 12582912.0f);  // bits 0..14 = C (see ccq_expand_bits)
-  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t P = (R[2 * h] & 0xFFFFu) | (R[2 * h + 1] << 16);  // C of bytes 2h, 2h+1
+    // P = C of byte 2h (low half) | C of byte 2h + 1 (high half): the magic-number add of
+    // ccq_expand_bits leaves C in bits 0..14, and the second add writes only its low 16 bits
+    // into the high half of the first result (SDWA destination select, other half kept).
+    uint32_t P = __float_as_uint(t[2 * h] + 12582912.0f);
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:DWORD"
+        : "+v"(P)
+        : "v"(t[2 * h + 1]), "v"(12582912.0f));
     // bit-shift decode: 6-bit states at shifts 9, 6, 3, 0 of each half
     const uint32_t q0 = pk_shr16(P, 9);  // C < 2^15: no bits above the field
     const uint32_t q1 = pk_shr16(P, 6) & 0x003F003Fu;
