@@ -265,7 +265,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 def moe_prefill(args):
     """One CCQ MoE layer at prefill size: 4096 tokens, top-8 of 64 experts, Zipf(1.1)-biased
-    routing.  Reports unpadded bf16 TFLOP/s (2 * pairs * 3 * hidden * inter per call)."""
+    routing.  `value` is unpadded bf16 TFLOP/s of the whole layer (2 * pairs * 3 * hidden * inter
+    per call, routing and combine included); the roofline is the gate+up kernel's, from HIP
+    events around its launches on the stream they run on."""
     import numpy as np
     import torch
 
@@ -281,7 +283,8 @@ def moe_prefill(args):
     ids_d, wts_d = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(wq.wq_moe_workspace_bytes(T, K, E, H, I), dtype=torch.uint8, device=dev)
-    flops = 2.0 * T * K * 3 * H * I
+    P = T * K
+    flops = 2.0 * P * 3 * H * I
     for _ in range(args.warmup):
         wq.wq_moe_ffn(x, ids_d, wts_d, g, u, dn, y=y, ws=ws)
     torch.cuda.synchronize()
@@ -293,7 +296,35 @@ def moe_prefill(args):
     torch.cuda.synchronize()
     ms = st.elapsed_time(en) / args.steps
     tf = flops / (ms * 1e-3) / 1e12
+
+    # the stages one by one (same kernels as wq_moe_ffn), each launch bracketed by events
+    off, pairs = wq.wq_moe_route(ids_d, E)
+    h = torch.empty((P, I), dtype=torch.bfloat16, device=dev)
+    d = torch.empty((P, H), dtype=torch.float32, device=dev)
+    stages = {"route": lambda: wq.wq_moe_route(ids_d, E),
+              "gate_up": lambda: wq.wq_moe_gate_up(x, off, pairs, K, g, u, h=h),
+              "down": lambda: wq.wq_moe_down(h, T, K, off, pairs, dn, d=d),
+              "combine": lambda: wq.wq_moe_combine(d, wts_d, y=y)}
+    stage_us = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(max(args.steps, 1)):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            fn()
+            a1.record()
+            evs.append((a0, a1))
+        torch.cuda.synchronize()
+        stage_us[name] = float(np.mean([a0.elapsed_time(a1) for a0, a1 in evs])) * 1e3
+    gu_flops = 2.0 * P * 2 * H * I
+    gu_tf = gu_flops / (stage_us["gate_up"] * 1e-6) / 1e12
+    dn_tf = 2.0 * P * H * I / (stage_us["down"] * 1e-6) / 1e12
     counts = np.bincount(ids.ravel(), minlength=E)
+    log(f"layer {ms * 1e3:.0f} us ({tf:.1f} TFLOP/s); stages: " +
+        ", ".join(f"{k} {v:.0f} us" for k, v in stage_us.items()) +
+        f"; gate+up {gu_tf:.1f} TFLOP/s, down {dn_tf:.1f} TFLOP/s")
     out = {"metric": "bf16 TFLOP/s (prefill MoE layer, CCQ g64)", "value": round(tf, 2),
            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -302,8 +333,13 @@ def moe_prefill(args):
                       "hidden": H, "inter": I, "routing": "zipf s=1.1",
                       "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())},
            "tokens_per_s": round(T / (ms * 1e-3), 1),
-           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}}
+           "stage_us": {k: round(v, 1) for k, v in stage_us.items()},
+           "down_tflops": round(dn_tf, 2),
+           "roofline": {"kernel": "tiled_kernel CCQ gate+up (MODE_GATEUP)", "bound": "mfma",
+                        "achieved": round(gu_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": None, "avg_launch_us": round(stage_us["gate_up"], 1),
+                        "algorithmic_flops_per_launch": gu_flops}}
     print(json.dumps(out), flush=True)
 
 
