@@ -64,10 +64,12 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens per sampled layer for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="moe_stack_decode",
-                    choices=["moe_stack_decode", "moe_prefill", "dense_decode", "copy_calibration"],
+                    choices=["moe_stack_decode", "moe_prefill", "dense_decode", "copy_calibration",
+                             "pages_shapes"],
                     help="moe_stack_decode (default): the 54-layer stack step; moe_prefill: one "
                          "CCQ MoE layer at 4096 tokens with Zipf-skewed routing; dense_decode: "
-                         "one 4096x4096 CCQ / 2-bit affine linear at 1, 8, 32 rows")
+                         "one 4096x4096 CCQ / 2-bit affine linear at 1, 8, 32 rows; pages_shapes: "
+                         "the GEMV and grouped-GEMM shapes of the CCQ paper's operator tables")
     return ap.parse_args()
 
 
@@ -110,6 +112,8 @@ def main():
         return dense_decode(args)
     if args.workload == "copy_calibration":
         return copy_calibration(args)
+    if args.workload == "pages_shapes":
+        return pages_shapes(args)
 
     import numpy as np
     import torch
@@ -387,6 +391,108 @@ def dense_decode(args):
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "dense_decode", "n": N, "k": Kd}, "results": res}
+    print(json.dumps(out), flush=True)
+
+
+# The operator tables of the CCQ paper's inference-performance section (execution time in ms on
+# one NVIDIA H20; quoted as context only, another machine's numbers): GEMV input x output at
+# M = 1 and 4 (columns WINT2-standard, CCQ) and grouped GEMM groups x output x input at M = 1,
+# 4, 16, 64 (columns W4A16, W2A16-CCQ).
+PAGES_GEMV_MS = {(4096, 4096, 1): (0.027, 0.034), (4096, 1024, 1): (0.015, 0.017),
+                 (8192, 8192, 1): (0.073, 0.090), (8192, 1024, 1): (0.019, 0.022),
+                 (4096, 4096, 4): (0.028, 0.035), (4096, 1024, 4): (0.015, 0.017),
+                 (8192, 8192, 4): (0.076, 0.104), (8192, 1024, 4): (0.019, 0.024)}
+PAGES_GROUPED_MS = {(7168, 512, 1): (0.030, 0.021), (1024, 7168, 1): (0.068, 0.058),
+                    (7168, 512, 4): (0.035, 0.027), (1024, 7168, 4): (0.199, 0.166),
+                    (7168, 512, 16): (0.071, 0.059), (1024, 7168, 16): (0.624, 0.527),
+                    (7168, 512, 64): (0.193, 0.161), (1024, 7168, 64): (1.628, 1.386)}
+
+
+def pages_shapes(args):
+    """The pages' operator shapes on this GPU.  GEMV: dense wq_gemm, input K x output N, M rows,
+    2-bit affine (the WINT2-standard column) and CCQ.  Grouped GEMM: 256 experts, M tokens each
+    routed to 8 distinct experts uniformly; output x input 1024 x 7168 is the fused gate+up
+    product (2 x 512 outputs per pair, wq_moe_gate_up) and 7168 x 512 the down product
+    (wq_moe_down), INT4 g64 (W4A16) and CCQ (W2A16).  Every call reads weights that are not in
+    the 256 MB last-level cache: GEMVs rotate over >= 1 GiB of weight copies, grouped products
+    over 64 routing tables (each touches 8 M of the 256 experts)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_only_bit_amd as wq
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    fields = ("codes", "scales", "zeros", "qscale", "super_scale", "code_scale", "code_zero")
+
+    def timed(fn, reps):
+        fn(0)
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for i in range(reps):
+            fn(i)
+        en.record()
+        torch.cuda.synchronize()
+        return st.elapsed_time(en) / reps * 1e3  # us
+
+    gemv = {}
+    for (k, n, m), (ms_w2, ms_ccq) in PAGES_GEMV_MS.items():
+        row = {}
+        for fmt, name in ((wq.FMT_INT2_AFFINE, "wint2"), (wq.FMT_CCQ2, "ccq")):
+            copies = []
+            while True:
+                arr = synth.random_packed_device(fmt, 1, n, k, 7000 + len(copies))
+                copies.append(wq.PackedWeight(fmt, n, k, 1, 64, *(arr.get(f) for f in fields), 32))
+                if copies[0].nbytes() * len(copies) >= (1 << 30):
+                    break
+            x = torch.from_numpy(synth.acts_bf16((m, k), 701, m, k).view(np.int16)).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            us = timed(lambda i: wq.wq_gemm(x, copies[i % len(copies)], y=y), max(args.steps, 1) * len(copies))
+            row[name] = {"us": round(us, 2), "GB/s": round(copies[0].nbytes() / (us * 1e-6) / 1e9, 1)}
+            del copies
+        row["pages_h20_ms"] = {"wint2_standard": ms_w2, "ccq": ms_ccq}
+        gemv[f"{k}x{n}_m{m}"] = row
+
+    grouped = {}
+    E, topk = 256, 8
+    for fmt, name, group in ((wq.FMT_INT4, "w4a16", 64), (wq.FMT_CCQ2, "w2a16_ccq", 64)):
+        g = synth.random_packed_device(fmt, E, 512, 7168, 7101, group=group)
+        u = synth.random_packed_device(fmt, E, 512, 7168, 7102, group=group)
+        dn = synth.random_packed_device(fmt, E, 7168, 512, 7103, group=group)
+        gw = wq.PackedWeight(fmt, 512, 7168, E, group, *(g.get(f) for f in fields), 32)
+        uw = wq.PackedWeight(fmt, 512, 7168, E, group, *(u.get(f) for f in fields), 32)
+        dw = wq.PackedWeight(fmt, 7168, 512, E, group, *(dn.get(f) for f in fields), 32)
+        per_expert_gu = (gw.nbytes() + uw.nbytes()) // E
+        per_expert_dn = dw.nbytes() // E
+        for m in (1, 4, 16, 64):
+            x = torch.from_numpy(synth.acts_bf16((m, 7168), 702, m).view(np.int16)).to(dev)
+            routes = []
+            for r in range(64):
+                ids, _ = synth.routing_uniform(m, topk, E, 703, m, r)
+                off, pairs = wq.wq_moe_route(torch.from_numpy(ids).to(dev), E)
+                routes.append((off, pairs, len(np.unique(ids))))
+            h = torch.empty((m * topk, 512), dtype=torch.bfloat16, device=dev)
+            d = torch.empty((m * topk, 7168), dtype=torch.float32, device=dev)
+            reps = max(args.steps, 1) * len(routes)
+            us_gu = timed(lambda i: wq.wq_moe_gate_up(x, routes[i % 64][0], routes[i % 64][1], topk, gw, uw, h=h), reps)
+            us_dn = timed(lambda i: wq.wq_moe_down(h, m, topk, routes[i % 64][0], routes[i % 64][1], dw, d=d), reps)
+            touched = float(np.mean([r[2] for r in routes]))
+            for (o, i_, us, per) in ((1024, 7168, us_gu, per_expert_gu), (7168, 512, us_dn, per_expert_dn)):
+                key = f"256x{o}x{i_}_m{m}"
+                grouped.setdefault(key, {})[name] = {"us": round(us, 2),
+                                                     "GB/s": round(touched * per / (us * 1e-6) / 1e9, 1)}
+                grouped[key]["pages_h20_ms"] = dict(zip(("w4a16", "w2a16_ccq"), PAGES_GROUPED_MS[(o, i_, m)]))
+                grouped[key]["experts_touched"] = round(touched, 1)
+        del gw, uw, dw
+        torch.cuda.empty_cache()
+    for key, row in list(gemv.items()) + list(grouped.items()):
+        log(key, json.dumps(row))
+    out = {"metric": "latency of the pages' operator shapes (us)", "value": gemv["4096x4096_m1"]["ccq"]["us"],
+           "unit": "us", "n_gpus": 1, "steps": args.steps, "higher_is_better": False, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": "pages_shapes"}, "gemv": gemv, "grouped_gemm": grouped,
+           "note": "pages_h20_ms are the pages' own H20 timings, context only"}
     print(json.dumps(out), flush=True)
 
 
