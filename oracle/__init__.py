@@ -30,8 +30,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-INT4, AFFINE2, CCQ = 1, 2, 3
+INT4, AFFINE2, CCQ, CCQ432, CCQ_HYBRID = 1, 2, 3, 4, 5
 CCQ_ZP = 32  # reading: weight zero point 2^(L-1) for L = 6
+CCQ432_ZP = 8  # reading: 2^(L-1) for the 4-bit states of (4,3,2)
+CCQ_HYBRID_ZP = 4  # reading: 2^(L-1) for the 3-bit states of (3,3,2)(3,4,2)
+ALG2_GROUP_BYTES = {CCQ432: 22, CCQ_HYBRID: 20}  # code bytes per 64-weight group
 
 
 def build(force: bool = True) -> str:
@@ -97,6 +100,7 @@ def lib():
             "orc_quant_affine2": (i32, [vp, i64, i64, vp, vp, vp]),
             "orc_ccq_search": (ctypes.c_uint32, [vp, ctypes.c_double, i32, vp]),
             "orc_quant_ccq": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
+            "orc_quant_alg2": (i32, [vp, i64, i64, i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -249,7 +253,7 @@ class Packed:
     scales: np.ndarray = None       # bf16 bits (INT4, affine)
     zeros: np.ndarray = None        # u8 (affine)
     qscale: np.ndarray = None       # u8, two 4-bit group scales per byte (CCQ)
-    super_scale: np.ndarray = None  # f32 per row (CCQ)
+    super_scale: np.ndarray = None  # f32 per row (all CCQ formats)
     code_scale: np.ndarray = None   # f32 per row (CCQ)
     code_zero: np.ndarray = None    # f32 per row (CCQ)
     zp: int = CCQ_ZP
@@ -279,8 +283,13 @@ class Packed:
         return tot
 
 
-def quantize(w, fmt: int, group: int = 64, refine: bool = True, zp: int = CCQ_ZP) -> Packed:
+def default_zp(fmt: int) -> int:
+    return {CCQ: CCQ_ZP, CCQ432: CCQ432_ZP, CCQ_HYBRID: CCQ_HYBRID_ZP}.get(fmt, CCQ_ZP)
+
+
+def quantize(w, fmt: int, group: int = 64, refine: bool = True, zp: int | None = None) -> Packed:
     """Quantize fp32 weights [n, k] or [E, n, k] with the oracle's quantizers."""
+    zp = default_zp(fmt) if zp is None else zp
     w = _c(w, np.float32)
     if w.ndim == 2:
         w = w[None]
@@ -317,7 +326,34 @@ def quantize(w, fmt: int, group: int = 64, refine: bool = True, zp: int = CCQ_ZP
         return Packed(CCQ, n, k, E, 64, codes.reshape(E, n, -1), qscale=qscale.reshape(E, n, -1),
                       super_scale=sup.reshape(E, n), code_scale=cs.reshape(E, n),
                       code_zero=cz.reshape(E, n), zp=zp)
+    if fmt in ALG2_GROUP_BYTES:
+        codes = np.zeros((E * n, G * ALG2_GROUP_BYTES[fmt]), np.uint8)
+        sup = np.zeros(E * n, np.float32)
+        rc = lib().orc_quant_alg2(_p(flat), E * n, k, fmt, zp, int(bool(refine)), _p(codes),
+                                  _p(sup))
+        if rc:
+            raise ValueError("bad CCQ (4,3,2) / hybrid shape")
+        return Packed(fmt, n, k, E, 64, codes.reshape(E, n, -1), super_scale=sup.reshape(E, n),
+                      zp=zp)
     raise ValueError(f"unknown format {fmt}")
+
+
+def alg2_pack(fmt: int, words, super_scale, zp: int | None = None) -> Packed:
+    """Packed (4,3,2) / hybrid weight from raw code words [E, n, G, P] (u8 values for
+    (4,3,2), P = 22; u16 values for the hybrid, P = 10, stored little endian)."""
+    words = np.asarray(words)
+    E, n, G, P = words.shape
+    if fmt == CCQ432:
+        assert P == 22
+        codes = words.astype(np.uint8).reshape(E, n, G * 22)
+    elif fmt == CCQ_HYBRID:
+        assert P == 10
+        codes = words.astype("<u2").reshape(E, n, G * 10).view(np.uint8)
+    else:
+        raise ValueError(f"not an Algorithm-2 format: {fmt}")
+    return Packed(fmt, n, 64 * G, E, 64, np.ascontiguousarray(codes),
+                  super_scale=_c(super_scale, np.float32).reshape(E, n),
+                  zp=default_zp(fmt) if zp is None else zp)
 
 
 def dequantize(p: Packed, expert: int = 0, n0: int = 0, n1: int | None = None) -> np.ndarray:

@@ -177,6 +177,12 @@ ORC_API double orc_ccq_bpw(int32_t T, int32_t g, int32_t N, int32_t scale_bits) 
 /*   format 3: CCQ (L,N,S) = (6,4,3) with code cluster: codes u8[E][n][k/4] (one clustered     */
 /*             code per 4 weights), qscale u8[E][n][ceil(k/128)] (two 4-bit group scales per   */
 /*             byte, low nibble = even group), super/code_scale/code_zero f32 [E][n], zp.       */
+/*   format 4: CCQ (4,3,2) without code cluster, 2.75 bpw: 22 u8 code words per 64-weight     */
+/*             group, codes u8[E][n][k/64*22]; the last word's low 4 bits hold the group's    */
+/*             quantized scale; super f32 [E][n], zp.                                         */
+/*   format 5: CCQ hybrid (3,3,2)+(3,4,2), 2.5 bpw: 10 u16 code words per group (little      */
+/*             endian), codes u8[E][n][k/64*20]; the last word's low 13 bits hold the group's */
+/*             quantized scale; super f32 [E][n], zp.                                         */
 /* ------------------------------------------------------------------------------------------ */
 
 typedef struct {
@@ -195,7 +201,7 @@ typedef struct {
   int32_t zp;
 } orc_weight;
 
-enum { ORC_INT4 = 1, ORC_AFFINE2 = 2, ORC_CCQ = 3 };
+enum { ORC_INT4 = 1, ORC_AFFINE2 = 2, ORC_CCQ = 3, ORC_CCQ432 = 4, ORC_CCQ_HYBRID = 5 };
 
 /* [E6.4] "Do it in code" (sign-extended 4-bit field) and "Math and notation" (x_hat = s(q-z)
  * with z = 0): W_hat = bf16(f32(q) * f32(s)). */
@@ -261,10 +267,45 @@ static uint16_t decode_ccq(const orc_weight* w, int64_t e, int64_t n, int64_t k)
   return f32_to_bf16(d);
 }
 
+/* [CCQ] section 3.5, "Dequantization without Code Cluster", with the (4,3,2) and hybrid
+ * (3,3,2)(3,4,2) rows of the dequantization-configuration table, and section 3.4 (scale
+ * compression: the group's quantized scale sits in the redundant bits of its last code word).
+ * For weight index i of a 64-weight group whose code words are W[0 .. P-1]:
+ *   s      = (W[P-1] & s_mask) * s_super                    (fp32 multiply)
+ *   u      = (W[i / p_w] >> shift[i % p_w]) & w_mask
+ *   W_hat  = bf16((u - zp) * s)                             (fp32 multiply, then bf16)
+ * with p_w the number of shifts.  (4,3,2): u8 words, P = 22, shifts (4,2,0), w_mask 0xF,
+ * s_mask 0xF.  Hybrid: u16 words, P = 10, shifts (13,11,9,6,4,2,0), w_mask 0x7, s_mask
+ * 0x1FFF.  Readings: a group's words are stored consecutively and groups consecutively along
+ * the row; u16 words are little endian; the states of a word are taken in the order of the
+ * shift list (the first state uses the highest shift). */
+static uint32_t alg2_word(const orc_weight* w, int64_t row, int64_t g, int64_t j) {
+  if (w->format == ORC_CCQ432) return w->codes[row * (w->k / 64) * 22 + g * 22 + j];
+  const uint8_t* b = w->codes + row * (w->k / 64) * 20 + g * 20 + 2 * j;
+  return (uint32_t)b[0] | ((uint32_t)b[1] << 8);
+}
+
+static uint16_t decode_alg2(const orc_weight* w, int64_t e, int64_t n, int64_t k) {
+  static const int32_t sh432[3] = {4, 2, 0};
+  static const int32_t shhyb[7] = {13, 11, 9, 6, 4, 2, 0};
+  const int hyb = w->format == ORC_CCQ_HYBRID;
+  const int32_t P = hyb ? 10 : 22, pw = hyb ? 7 : 3;
+  const uint32_t wmask = hyb ? 0x7u : 0xFu, smask = hyb ? 0x1FFFu : 0xFu;
+  const int32_t* shift = hyb ? shhyb : sh432;
+  int64_t row = e * w->n + n;
+  int64_t g = k / 64, i = k % 64;
+  float s = (float)(alg2_word(w, row, g, P - 1) & smask) * w->super_scale[row];
+  int32_t u = (int32_t)((alg2_word(w, row, g, i / pw) >> shift[i % pw]) & wmask);
+  float d = (float)(u - w->zp) * s;
+  return f32_to_bf16(d);
+}
+
 static uint16_t decode_one(const orc_weight* w, int64_t e, int64_t n, int64_t k) {
   switch (w->format) {
     case ORC_INT4: return decode_int4(w, e, n, k);
     case ORC_AFFINE2: return decode_affine2(w, e, n, k);
+    case ORC_CCQ432:
+    case ORC_CCQ_HYBRID: return decode_alg2(w, e, n, k);
     default: return decode_ccq(w, e, n, k);
   }
 }
@@ -272,7 +313,9 @@ static uint16_t decode_one(const orc_weight* w, int64_t e, int64_t n, int64_t k)
 static int check_weight(const orc_weight* w) {
   if (w->k <= 0 || w->n <= 0 || w->k % 64 != 0) return -1;
   if (w->format == ORC_INT4) return (w->group == 64 || w->group == 0) ? 0 : -1;
-  if (w->format == ORC_AFFINE2 || w->format == ORC_CCQ) return w->group == 64 ? 0 : -1;
+  if (w->format == ORC_AFFINE2 || w->format == ORC_CCQ || w->format == ORC_CCQ432 ||
+      w->format == ORC_CCQ_HYBRID)
+    return w->group == 64 ? 0 : -1;
   return -1;
 }
 
@@ -637,5 +680,164 @@ ORC_API int32_t orc_quant_ccq(const float* w, int64_t n, int64_t k, int32_t zp, 
   }
   free(full);
   free(sdec);
+  return 0;
+}
+
+/* [CCQ] section 3.1 (Algorithm "Convolutional Code Quantization"), section 3.2 (hybrid
+ * encoding) and section 3.4 (scale optimization, scale compression into redundant bits), for
+ * the two configurations that need no code cluster, per output row with groups of 64 along k:
+ *   fmt ORC_CCQ432:     (L,N,S) = (4,3,2): 22 u8 codes per group, 3 weights per code
+ *                       (weights 3i .. 3i+2 in code i); the last code holds weight 63 in its
+ *                       high state and the 4-bit quantized scale in its low 4 bits.
+ *   fmt ORC_CCQ_HYBRID: (3,3,2) followed by (3,4,2) in one u16 word: 7 weights per word
+ *                       (weights 7i .. 7i+6 in word i: three 3-bit states at bits 15..9, then
+ *                       four at bits 8..0); the last word holds weight 63 in bits 15..13 and
+ *                       the 13-bit quantized scale in bits 12..0.
+ * Steps (readings stated where the pages leave a choice):
+ *   1. group scale s_g = absmax_g / (2^(L-1) - 1) (7 for L = 4, 3 for L = 3); zp = 2^(L-1)
+ *      is the caller's (8 or 4);
+ *   2. scale compression: super = max_g s_g / s_mask per row (s_mask = 15 or 8191; a row of
+ *      zeros gets super = 1), s_q = clip(round(s_g / super), 1, s_mask), s = fl(s_q * super);
+ *   3. codebook search: every code of a configuration decodes by bit shifts to N states; the
+ *      stored code is the argmin over all 2^T codes of sum_j (v_j - (state_j - zp) * s)^2,
+ *      ties to the smallest code (exhaustive: at most 2^9 candidates);
+ *   4. the last code of a group: its states past weight 63 are padding and its remaining
+ *      bits carry s_q, so only weight 63's state is searched;
+ *   5. refine != 0: one pass of the least-squares scale update S* = sum W Wq / sum Wq^2 over
+ *      the group's decoded states Wq = state - zp (section 3.4), re-quantized as in step 2,
+ *      re-searched, and kept only when the group's squared error drops.
+ * codes: u8[n][k/64 * 22] or u8[n][k/64 * 20] (u16 little endian); super_scale f32[n]. */
+static double alg2_search(int hyb, const double* v, int nv, double s, int32_t zp,
+                          uint32_t* best_code) {
+  /* nv = number of real weights in v (the code's remaining states are padding). */
+  const int L = hyb ? 3 : 4;
+  double total = 0.0;
+  uint32_t word = 0;
+  /* the parts of one stored word: (bits, states, shift of the lowest state) */
+  int parts = hyb ? 2 : 1;
+  int pos = 0;
+  for (int p = 0; p < parts; ++p) {
+    int N = hyb ? (p == 0 ? 3 : 4) : 3;
+    int T = L + (N - 1) * 2;
+    int base = hyb ? (p == 0 ? 9 : 0) : 0;
+    uint32_t bc = 0;
+    double bcost = INFINITY;
+    for (uint32_t c = 0; c < (1u << T); ++c) {
+      double cost = 0.0;
+      for (int j = 0; j < N; ++j) {
+        if (pos + j >= nv) break;
+        int32_t u = (int32_t)((c >> (2 * (N - 1 - j))) & ((1u << L) - 1u));
+        double r = v[pos + j] - (double)(u - zp) * s;
+        cost += r * r;
+      }
+      if (cost < bcost) { bcost = cost; bc = c; }
+    }
+    word |= bc << base;
+    total += bcost;
+    pos += N;
+  }
+  *best_code = word;
+  return total;
+}
+
+/* Encode one group (64 weights) with decode scale s; returns the squared error. */
+static double alg2_encode_group(int hyb, const float* wg, double s, int32_t zp, uint32_t sq,
+                                uint32_t* words) {
+  const int per = hyb ? 7 : 3, P = hyb ? 10 : 22;
+  double err = 0.0;
+  for (int i = 0; i < P; ++i) {
+    double v[7];
+    int nv = 0;
+    for (int j = 0; j < per; ++j)
+      if (i * per + j < 64) v[nv++] = (double)wg[i * per + j];
+    uint32_t code;
+    if (i < P - 1) {
+      err += alg2_search(hyb, v, nv, s, zp, &code);
+    } else {
+      /* weight 63 alone in the high state; the scale fills the low bits */
+      const int L = hyb ? 3 : 4, top = hyb ? 13 : 4;
+      double bcost = INFINITY;
+      uint32_t bu = 0;
+      for (uint32_t u = 0; u < (1u << L); ++u) {
+        double r = v[0] - (double)((int32_t)u - zp) * s;
+        if (r * r < bcost) { bcost = r * r; bu = u; }
+      }
+      err += bcost;
+      code = (bu << top) | sq;
+    }
+    words[i] = code;
+  }
+  return err;
+}
+
+ORC_API int32_t orc_quant_alg2(const float* w, int64_t n, int64_t k, int32_t fmt, int32_t zp,
+                               int32_t refine, uint8_t* codes, float* super_scale) {
+  if (k % 64 || (fmt != ORC_CCQ432 && fmt != ORC_CCQ_HYBRID)) return -1;
+  const int hyb = fmt == ORC_CCQ_HYBRID;
+  const int64_t G = k / 64;
+  const int P = hyb ? 10 : 22, bytes = hyb ? 20 : 22;
+  const double lev = hyb ? 3.0 : 7.0;
+  const uint32_t smask = hyb ? 0x1FFFu : 0xFu;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t r = 0; r < n; ++r) {
+    const float* row = w + r * k;
+    double smax = 0.0;
+    for (int64_t g = 0; g < G; ++g) {
+      double amax = 0.0;
+      for (int i = 0; i < 64; ++i) amax = fmax(amax, fabs((double)row[g * 64 + i]));
+      smax = fmax(smax, amax / lev);
+    }
+    float sup = (float)(smax / (double)smask);
+    if (!(sup > 0.0f)) sup = 1.0f;
+    super_scale[r] = sup;
+    for (int64_t g = 0; g < G; ++g) {
+      const float* wg = row + g * 64;
+      double amax = 0.0;
+      for (int i = 0; i < 64; ++i) amax = fmax(amax, fabs((double)wg[i]));
+      double sqd = nearbyint((amax / lev) / (double)sup);
+      if (sqd < 1) sqd = 1;
+      if (sqd > (double)smask) sqd = (double)smask;
+      uint32_t sq = (uint32_t)sqd;
+      uint32_t words[22];
+      double err = alg2_encode_group(hyb, wg, (double)((float)sq * sup), zp, sq, words);
+      if (refine) {
+        /* least-squares scale for the chosen states (section 3.4, scale optimization) */
+        const int per = hyb ? 7 : 3;
+        static const int32_t sh432[3] = {4, 2, 0};
+        static const int32_t shhyb[7] = {13, 11, 9, 6, 4, 2, 0};
+        double num = 0.0, den = 0.0;
+        for (int i = 0; i < 64; ++i) {
+          uint32_t u = (words[i / per] >> (hyb ? shhyb[i % per] : sh432[i % per])) &
+                       (hyb ? 0x7u : 0xFu);
+          double q = (double)((int32_t)u - zp);
+          num += (double)wg[i] * q;
+          den += q * q;
+        }
+        if (den > 0.0 && num > 0.0) {
+          double s2 = nearbyint((num / den) / (double)sup);
+          if (s2 < 1) s2 = 1;
+          if (s2 > (double)smask) s2 = (double)smask;
+          uint32_t sq2 = (uint32_t)s2;
+          if (sq2 != sq) {
+            uint32_t w2[22];
+            double e2 = alg2_encode_group(hyb, wg, (double)((float)sq2 * sup), zp, sq2, w2);
+            if (e2 < err) {
+              err = e2;
+              memcpy(words, w2, sizeof(words));
+            }
+          }
+        }
+      }
+      uint8_t* dst = codes + r * G * bytes + g * bytes;
+      for (int i = 0; i < P; ++i) {
+        if (hyb) {
+          dst[2 * i] = (uint8_t)(words[i] & 0xFFu);
+          dst[2 * i + 1] = (uint8_t)(words[i] >> 8);
+        } else {
+          dst[i] = (uint8_t)words[i];
+        }
+      }
+    }
+  }
   return 0;
 }
