@@ -22,6 +22,19 @@
  *                             u  = (C >> (9 - 3*(k%4))) & 0x3F
  *                             s  = f32(s_q) * super_scale           (s_q: 4-bit group scale)
  *                             x_hat = bf16(f32(u - zp) * s)
+ *       WQ_FMT_CCQ432       convolutional code (L,N,S) = (4,3,2) without code cluster, 2.75 bpw
+ *       WQ_FMT_CCQ_HYBRID   hybrid convolutional code (3,3,2)+(3,4,2) in 16-bit words, 2.5 bpw
+ *                           (CCQ paper, section 3.2 hybrid encoding, section 3.4 scale
+ *                           compression, section 3.5 algorithm "Dequantization without Code
+ *                           Cluster" and the table of dequantization configurations).  A group
+ *                           of 64 weights is P code words W[0..P-1]; weight i of the group is
+ *                             u  = (W[i / p] >> shift[i % p]) & w_mask
+ *                             s  = f32(W[P-1] & s_mask) * super_scale
+ *                             x_hat = bf16(f32(u - zp) * s)
+ *                           (4,3,2): u8 words, P = 22, p = 3, shifts 4,2,0, w_mask 0xF,
+ *                           s_mask 0xF.  Hybrid: u16 words, P = 10, p = 7, shifts
+ *                           13,11,9,6,4,2,0, w_mask 0x7, s_mask 0x1FFF.  The last word carries
+ *                           weight 63 in its top state and the group scale in its low bits.
  *
  * Layouts (every matrix is W[n][k], k contiguous, y = x W^T; an MoE tensor adds a leading
  * expert dimension; group = 64 along k; G = k / 64):
@@ -30,6 +43,10 @@
  *   CCQ2:   codes u8[E][n][k/4]; qscale u8[E][n][(G+1)/2], two 4-bit group scales per byte,
  *           the even group in the low nibble; super_scale, code_scale, code_zero f32[E][n];
  *           zp (32 for the symmetric 6-bit states).
+ *   CCQ432: codes u8[E][n][G*22] (each group's 22 words consecutive, groups in k order);
+ *           super_scale f32[E][n]; zp (8 for the 4-bit states).
+ *   CCQ_HYBRID: codes u8[E][n][G*20] (each group's 10 u16 words, little endian);
+ *           super_scale f32[E][n]; zp (4 for the 3-bit states).
  *
  * Conventions for every call below:
  *   - Every pointer inside wq_weight and every tensor argument of a compute call is DEVICE
@@ -46,7 +63,9 @@
  *     wq_gemm / wq_moe_ffn need a CCQ zero point of 0 or a power of two (the kernels form
  *     (u - zp) * s as fma(u, s, -zp * s), the same single rounding when zp * s is exact) and
  *     2-bit affine zero points below 256.  The decoded weights the products use are the
- *     same bits wq_dequantize returns.
+ *     same bits wq_dequantize returns, except that a weight the definition makes -0 (a zero
+ *     group scale times a negative state offset) enters the products as +0, which no sum
+ *     starting from +0 can tell apart.
  *   - Sizes are element counts (int64).  Device pointers must be 16-byte aligned.
  */
 #ifndef WQ_H
@@ -69,7 +88,13 @@ typedef enum {
   WQ_ERR_HIP = -6          /* the HIP runtime reported an error at launch               */
 } wq_status;
 
-typedef enum { WQ_FMT_INT4 = 1, WQ_FMT_INT2_AFFINE = 2, WQ_FMT_CCQ2 = 3 } wq_format;
+typedef enum {
+  WQ_FMT_INT4 = 1,
+  WQ_FMT_INT2_AFFINE = 2,
+  WQ_FMT_CCQ2 = 3,
+  WQ_FMT_CCQ432 = 4,
+  WQ_FMT_CCQ_HYBRID = 5
+} wq_format;
 
 /* A packed weight tensor [experts][n][k] in device memory (see layouts above). */
 typedef struct {
@@ -82,10 +107,10 @@ typedef struct {
   const uint16_t* scales;    /* bf16 bits; INT4 and AFFINE                                 */
   const uint8_t* zeros;      /* AFFINE                                                     */
   const uint8_t* qscale;     /* CCQ2                                                       */
-  const float* super_scale;  /* CCQ2                                                       */
+  const float* super_scale;  /* CCQ2, CCQ432, CCQ_HYBRID                                   */
   const float* code_scale;   /* CCQ2                                                       */
   const float* code_zero;    /* CCQ2                                                       */
-  int32_t zp;                /* CCQ2 weight zero point                                     */
+  int32_t zp;                /* CCQ weight zero point (all three CCQ formats)              */
 } wq_weight;
 
 /* Decode every weight to bf16, out[e][n][k] (device, bf16 bits).  Bit-exact with the

@@ -15,7 +15,11 @@ import numpy as np
 
 SEED = 20261203
 
-FMT_INT4, FMT_AFFINE2, FMT_CCQ = 1, 2, 3
+FMT_INT4, FMT_AFFINE2, FMT_CCQ, FMT_CCQ432, FMT_CCQ_HYBRID = 1, 2, 3, 4, 5
+_GROUP_BYTES = {FMT_CCQ432: 22, FMT_CCQ_HYBRID: 20}
+# super scale that puts a uniform group-scale field at the magnitude of a N(0, 0.02) group:
+# absmax ~ 3 std over (2^(L-1) - 1) levels, spread over the field's range
+_ALG2_SUPER = {FMT_CCQ432: 0.02 * 3.0 / 7.0 / 15.0, FMT_CCQ_HYBRID: 0.02 * 3.0 / 3.0 / 8191.0}
 
 
 def rng(*path: int) -> np.random.Generator:
@@ -87,6 +91,9 @@ def packed_layout(fmt: int, experts: int, n: int, k: int, group: int = 64) -> di
                 "super_scale": ((experts, n), np.float32),
                 "code_scale": ((experts, n), np.float32),
                 "code_zero": ((experts, n), np.float32)}
+    if fmt in _GROUP_BYTES:
+        return {"codes": ((experts, n, G * _GROUP_BYTES[fmt]), np.uint8),
+                "super_scale": ((experts, n), np.float32)}
     raise ValueError(fmt)
 
 
@@ -94,7 +101,9 @@ def random_packed(fmt: int, experts: int, n: int, k: int, *path: int, group: int
     """Random packed weights on the host: uniform code bytes; scales of the magnitude a
     N(0, 0.02) weight would get (INT4 ~ 0.02*U(2,3)/7, affine ~ 0.02*U(3,5)/3 with zero
     points in 0..3); CCQ group scales uniform in 1..15, super scale 0.02*3/31/15, code scale
-    U(64, 128) and an integral code zero that keeps 255*scale + zero below 2^15."""
+    U(64, 128) and an integral code zero that keeps 255*scale + zero below 2^15.  The CCQ
+    formats without code cluster draw every code byte (scale fields included) uniformly, with
+    a super scale of the magnitude of the field's mean."""
     g = rng(*path)
     lay = packed_layout(fmt, experts, n, k, group)
     out = {}
@@ -104,6 +113,9 @@ def random_packed(fmt: int, experts: int, n: int, k: int, *path: int, group: int
     elif fmt == FMT_AFFINE2:
         out["scales"] = bf16_bits(0.02 * g.uniform(3.0, 5.0, size=lay["scales"][0]) / 3.0)
         out["zeros"] = g.integers(0, 4, size=lay["zeros"][0], dtype=np.uint8)
+    elif fmt in _GROUP_BYTES:
+        shp = lay["super_scale"][0]
+        out["super_scale"] = (2.0 * _ALG2_SUPER[fmt] * g.uniform(0.8, 1.2, size=shp)).astype(np.float32)
     else:
         lo = g.integers(1, 16, size=lay["qscale"][0], dtype=np.uint8)
         hi = g.integers(1, 16, size=lay["qscale"][0], dtype=np.uint8)
@@ -139,6 +151,8 @@ def random_packed_device(fmt: int, experts: int, n: int, k: int, seed: int, devi
         out["scales"] = (0.02 * u(lay["scales"][0], 3.0, 5.0) / 3.0).to(torch.bfloat16).view(torch.int16)
         out["zeros"] = torch.randint(0, 4, lay["zeros"][0], dtype=torch.uint8, device=device,
                                      generator=gen)
+    elif fmt in _GROUP_BYTES:
+        out["super_scale"] = (2.0 * _ALG2_SUPER[fmt]) * u(lay["super_scale"][0], 0.8, 1.2)
     else:
         lo = torch.randint(1, 16, lay["qscale"][0], dtype=torch.uint8, device=device, generator=gen)
         hi = torch.randint(1, 16, lay["qscale"][0], dtype=torch.uint8, device=device, generator=gen)

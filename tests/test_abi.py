@@ -89,6 +89,11 @@ def _weight(wq, **kw):
     (dict(n=0), -1),
     (dict(format=1, group=128, scales=0x6000), -2),
     (dict(format=2, scales=0x6000, zeros=None), -1),
+    (dict(format=4, super_scale=None), -1),   # (4,3,2) needs its super scale
+    (dict(format=5, super_scale=0x3004), -3),  # misaligned super scale
+    (dict(format=5, zp=6), -2),               # hybrid zero point not a power of two
+    (dict(format=4, group=0), -2),
+    (dict(format=6), -2),
 ])
 def test_gemm_rejects_bad_descriptors_without_launch(wq, kw, status):
     L = wq.lib()

@@ -16,7 +16,9 @@ from wq_testutil import assert_close, to_device, torch_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
-FMTS = {"int4": oracle.INT4, "affine2": oracle.AFFINE2, "ccq": oracle.CCQ}
+FMTS = {"int4": oracle.INT4, "affine2": oracle.AFFINE2, "ccq": oracle.CCQ,
+        "ccq432": oracle.CCQ432, "ccqh": oracle.CCQ_HYBRID}
+ALL = ["int4", "int4pc", "affine2", "ccq", "ccq432", "ccqh"]
 
 
 def _say(*a):
@@ -40,18 +42,27 @@ def _quant(fmt, shape, seed, group=64):
     return oracle.quantize(w, fmt, group=group)
 
 
+def _product_bits(decoded):
+    """What a product with identity activations returns for decoded weight bits: the sum
+    starts at +0, so a -0 weight (a zero group scale times a state below the zero point)
+    comes back as +0."""
+    out = np.array(decoded, copy=True)
+    out[out == 0x8000] = 0
+    return out
+
+
 def _random_packed(fmt, E, n, k, seed, group=64):
     arr = synth.random_packed(fmt, E, n, k, *seed, group=group)
     return oracle.Packed(fmt, n, k, E, group, arr.get("codes"), arr.get("scales"), arr.get("zeros"),
                          arr.get("qscale"), arr.get("super_scale"), arr.get("code_scale"),
-                         arr.get("code_zero"), 32)
+                         arr.get("code_zero"), oracle.default_zp(fmt))
 
 
 # ---------------------------------------------------------------------------------------------
 # Dequantize: bit-exact
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+@pytest.mark.parametrize("name", ALL)
 @pytest.mark.parametrize("src", ["quantized", "random"])
 def test_dequantize_bit_exact(wq, name, src):
     fmt = FMTS["int4" if name == "int4pc" else name]
@@ -66,6 +77,22 @@ def test_dequantize_bit_exact(wq, name, src):
     for e in range(E):
         ref = oracle.dequantize(p, e)
         assert np.array_equal(got[e], ref), f"expert {e}: {(got[e] != ref).sum()} mismatches"
+
+
+@pytest.mark.parametrize("name", ["ccq432", "ccqh"])
+def test_dequantize_alg2_every_word_value(wq, name):
+    # every u8 / u16 word value in every non-last position class, random last words (weight 63
+    # and the group scale field), odd group count (groups start 2 bytes into a dword)
+    fmt = FMTS[name]
+    P, nvals = (22, 256) if name == "ccq432" else (10, 65536)
+    g = np.random.default_rng(31)
+    n, G = 16, 5 if name == "ccq432" else 457
+    body = np.resize(np.arange(nvals), n * G * (P - 1)).reshape(n, G, P - 1)
+    words = np.concatenate([body, g.integers(0, nvals, (n, G, 1))], axis=2)
+    sup = g.uniform(1e-5, 1e-3, (1, n)).astype(np.float32)
+    p = oracle.alg2_pack(fmt, words[None], sup)
+    got = torch_bf16_bits(wq.wq_dequantize(to_device(p)))[0]
+    assert np.array_equal(got, oracle.dequantize(p))
 
 
 def test_dequantize_ccq_every_code(wq):
@@ -109,7 +136,7 @@ def test_dequantize_ccq_rounding_and_clamp_edges(wq):
 DENSE_SHAPES = [(80, 576), (128, 1024), (512, 512)]
 
 
-@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+@pytest.mark.parametrize("name", ALL)
 @pytest.mark.parametrize("nk", DENSE_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
 @pytest.mark.parametrize("m", [1, 3, 16, 17, 32, 33, 70, 150, 276])
 def test_gemm_parity(wq, name, nk, m):
@@ -138,7 +165,7 @@ def test_gemm_deterministic(wq):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+@pytest.mark.parametrize("name", ALL)
 def test_tiled_gemm_repeatable_short_k(wq, name):
     # Many activation rows (tiled kernel) with short K: every step of the pipeline is a
     # prologue or tail step.  Repeated launches must give identical bits within tolerance of
@@ -164,7 +191,7 @@ def test_tiled_gemm_repeatable_short_k(wq, name):
             assert np.array_equal(y, first), f"tiled {name} k={k}: run {rep} differs from run 0"
 
 
-@pytest.mark.parametrize("name", ["int4", "int4pc", "affine2", "ccq"])
+@pytest.mark.parametrize("name", ALL)
 def test_gemm_decodes_every_weight_bit_exact(wq, name):
     # Identity activations: row m of x = e_(c0+m) makes y[m][n] = W_hat[n][c0+m], one exact
     # product rounded back to the same bf16 -- so the product path's decode of every weight
@@ -181,7 +208,25 @@ def test_gemm_decodes_every_weight_bit_exact(wq, name):
         x = np.zeros((32, k), np.uint16)
         x[np.arange(32), c0 + np.arange(32)] = 0x3F80
         y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
-        assert np.array_equal(y.T, ref[:, c0:c0 + 32]), f"columns {c0}..{c0 + 31}"
+        assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + 32])), f"columns {c0}..{c0 + 31}"
+
+
+@pytest.mark.parametrize("name", ["ccq432", "ccqh"])
+def test_gemm_alg2_random_words_bit_exact(wq, name):
+    # uniformly random code words (any scale field, any states) through the product path's
+    # decode; k = 576 gives 9 groups per row, so (4,3,2) groups start at both byte offsets
+    import torch
+
+    fmt = FMTS[name]
+    n, k = 48, 576
+    p = _random_packed(fmt, 1, n, k, (32, fmt))
+    ref = oracle.dequantize(p)
+    d = to_device(p)
+    for c0 in range(0, k, 32):
+        x = np.zeros((32, k), np.uint16)
+        x[np.arange(32), c0 + np.arange(32)] = 0x3F80
+        y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
+        assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + 32])), f"columns {c0}..{c0 + 31}"
 
 
 # ---------------------------------------------------------------------------------------------
@@ -215,6 +260,10 @@ MOE_CASES = [
     ("ccq", 4, 256, 192, 64, 2),        # tiled, 32 rows per expert on average
     ("int4pc", 8, 512, 320, 200, 4),    # tiled, ragged row tiles
     ("affine2", 4, 320, 128, 96, 2),    # tiled
+    ("ccq432", 8, 320, 192, 12, 2),
+    ("ccqh", 8, 576, 320, 40, 4),
+    ("ccq432", 4, 576, 192, 64, 2),     # 32 rows per expert on average
+    ("ccqh", 8, 512, 320, 200, 4),
 ]
 
 
@@ -278,7 +327,7 @@ def test_tiled_gemm_decodes_every_weight_bit_exact(wq):
     # W_hat[n][c0 + m] exactly, for every weight, in every format.
     import torch
 
-    for name in ("ccq", "int4", "int4pc", "affine2"):
+    for name in ALL:
         fmt = FMTS["int4" if name == "int4pc" else name]
         group = 0 if name == "int4pc" else 64
         n, k = 136, 320
@@ -290,7 +339,7 @@ def test_tiled_gemm_decodes_every_weight_bit_exact(wq):
             x = np.zeros((w, k), np.uint16)
             x[np.arange(w), c0 + np.arange(w)] = 0x3F80
             y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
-            assert np.array_equal(y.T, ref[:, c0:c0 + w]), f"{name} columns {c0}.."
+            assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + w])), f"{name} columns {c0}.."
 
 
 @pytest.mark.parametrize("name", ["ccq", "int4pc"])
@@ -341,4 +390,4 @@ def test_gemm_ccq_clamped_rows_bit_exact(wq):
             x = np.zeros((w, k), np.uint16)
             x[np.arange(w), c0 + np.arange(w)] = 0x3F80
             y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
-            assert np.array_equal(y.T, ref[:, c0:c0 + w]), (m, c0)
+            assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + w])), (m, c0)

@@ -33,13 +33,31 @@ wq_status hip_status(hipError_t e, const char* what) {
   return fail(WQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Formats the tiled (many-row) kernels implement; the others run the decode-streaming kernels
+// for every row count.
+bool has_tiled(int32_t f) { return f == WQ_FMT_INT4 || f == WQ_FMT_INT2_AFFINE || f == WQ_FMT_CCQ2; }
+
+bool is_ccq(int32_t f) {
+  return f == WQ_FMT_CCQ2 || f == WQ_FMT_CCQ432 || f == WQ_FMT_CCQ_HYBRID;
+}
+
+// Bytes of one packed row of k weights.
+int64_t row_code_bytes(const wq_weight* w) {
+  switch (w->format) {
+    case WQ_FMT_INT4: return w->k / 2;
+    case WQ_FMT_CCQ432: return w->k / 64 * 22;
+    case WQ_FMT_CCQ_HYBRID: return w->k / 64 * 20;
+    default: return w->k / 4;
+  }
+}
+
 // The product kernels decode CCQ weights as fma(u, s, -zp*s), exact when zp*s is exact: zp
-// must then be zero or a power of two (the format's zero point is 32).
+// must then be zero or a power of two (the formats' zero points are 32, 8 and 4).
 // The product kernels also address one expert's matrix with 32-bit byte offsets.
 wq_status check_product_zp(const wq_weight* w, const char* what) {
-  if (w->format == WQ_FMT_CCQ2 && (w->zp & (w->zp - 1)) != 0)
+  if (is_ccq(w->format) && (w->zp & (w->zp - 1)) != 0)
     return fail(WQ_ERR_UNSUPPORTED, "%s: products need a CCQ zero point of 0 or a power of two", what);
-  const int64_t row_bytes = (w->format == WQ_FMT_INT4) ? w->k / 2 : w->k / 4;
+  const int64_t row_bytes = row_code_bytes(w);
   if (w->n * row_bytes >= (1ll << 31))
     return fail(WQ_ERR_UNSUPPORTED, "%s: one expert's codes must be below 2 GiB", what);
   return WQ_OK;
@@ -75,6 +93,15 @@ wq_status check_weight(const wq_weight* w, const char* what) {
       if (!aligned16(w->qscale) || !aligned16(w->super_scale) || !aligned16(w->code_scale) ||
           !aligned16(w->code_zero))
         return fail(WQ_ERR_ALIGN, "%s: CCQ scale arrays not 16-byte aligned", what);
+      if (w->zp < 0 || w->zp > 127)
+        return fail(WQ_ERR_UNSUPPORTED, "%s: CCQ zero point must lie in 0..127", what);
+      break;
+    case WQ_FMT_CCQ432:
+    case WQ_FMT_CCQ_HYBRID:
+      if (w->group != 64) return fail(WQ_ERR_UNSUPPORTED, "%s: CCQ needs group 64", what);
+      if (!w->super_scale) return fail(WQ_ERR_ARG, "%s: null super_scale", what);
+      if (!aligned16(w->super_scale))
+        return fail(WQ_ERR_ALIGN, "%s: super_scale not 16-byte aligned", what);
       if (w->zp < 0 || w->zp > 127)
         return fail(WQ_ERR_UNSUPPORTED, "%s: CCQ zero point must lie in 0..127", what);
       break;
@@ -200,7 +227,7 @@ wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y,
   if (!aligned16(x) || !aligned16(y)) return fail(WQ_ERR_ALIGN, "wq_gemm: x or y not 16-byte aligned");
   if (m > (1ll << 31)) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: m must be below 2^31");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (m > kSkinnyMaxRows) {
+  if (m > kSkinnyMaxRows && has_tiled(w->format)) {
     wq::TiledArgs t{};
     t.w0 = dev_weight(w);
     t.w1 = t.w0;
@@ -285,8 +312,8 @@ int moe_row_tiles(int64_t t, int32_t topk, int64_t experts) {
   return ((double)t * topk / (double)experts <= 8.0) ? 1 : 2;
 }
 
-bool moe_tiled(int64_t t, int32_t topk, int64_t experts) {
-  return (double)t * topk / (double)experts >= kMoeTiledRows;
+bool moe_tiled(const wq_weight* w, int64_t t, int32_t topk) {
+  return has_tiled(w->format) && (double)t * topk / (double)w->experts >= kMoeTiledRows;
 }
 
 int64_t moe_tile_bound(int64_t t, int32_t topk, int64_t experts) {
@@ -307,7 +334,7 @@ wq::TiledArgs moe_tiled_args(const int32_t* offsets, const int32_t* sorted, int3
 hipError_t run_gate_up(const uint16_t* x, int64_t t, const int32_t* offsets, const int32_t* sorted,
                        int32_t topk, const wq_weight* gate, const wq_weight* up, uint16_t* h,
                        hipStream_t s) {
-  if (moe_tiled(t, topk, gate->experts)) {
+  if (moe_tiled(gate, t, topk)) {
     wq::TiledArgs a = moe_tiled_args(offsets, sorted, topk, gate->experts);
     a.w0 = dev_weight(gate);
     a.w1 = dev_weight(up);
@@ -337,7 +364,7 @@ hipError_t run_gate_up(const uint16_t* x, int64_t t, const int32_t* offsets, con
 
 hipError_t run_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* offsets,
                     const int32_t* sorted, const wq_weight* down, float* d, hipStream_t s) {
-  if (moe_tiled(t, topk, down->experts)) {
+  if (moe_tiled(down, t, topk)) {
     wq::TiledArgs a = moe_tiled_args(offsets, sorted, topk, down->experts);
     a.w0 = dev_weight(down);
     a.w1 = a.w0;

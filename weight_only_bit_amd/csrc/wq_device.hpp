@@ -17,7 +17,12 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum { FMT_INT4 = 1, FMT_AFFINE2 = 2, FMT_CCQ2 = 3 };
+enum { FMT_INT4 = 1, FMT_AFFINE2 = 2, FMT_CCQ2 = 3, FMT_CCQ432 = 4, FMT_CCQH = 5 };
+
+// The CCQ formats without code cluster: the group scale rides in the last code word.
+__host__ __device__ constexpr bool is_alg2(int f) { return f == FMT_CCQ432 || f == FMT_CCQH; }
+// Code bytes of one 64-weight group: 22 u8 words ((4,3,2)) or 10 u16 words (hybrid).
+__host__ __device__ constexpr int alg2_group_bytes(int f) { return f == FMT_CCQ432 ? 22 : 20; }
 
 // Device view of a packed weight [experts][n][k] (pointers already offset to expert 0).
 struct DevWeight {
@@ -96,6 +101,8 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // zero point times a bf16 scale, INT4's 8 * s).  So one instruction converts and scales a
 // weight, and 16-bit packed shifts place two codes per dword.  For c == z the result is +0
 // where the two-step form gives 0 * s: the same bits for s >= 0 (scales are non-negative).
+// For s == 0 (a zero group-scale field) and c < z the two-step form gives -0 and this one +0;
+// no product can tell them apart (every accumulation starts at +0).
 // Requires f16 subnormals to be kept (the default float mode) and |s| < 2^100.
 // ---------------------------------------------------------------------------------------------
 
@@ -184,6 +191,63 @@ __device__ __forceinline__ void affine2_decode16(uint32_t w, float s24, float mz
     p[j] = cvt_pk_bf16(mix_lo(q[2 * j], s24, mzs), mix_lo(q[2 * j + 1], s24, mzs));
     p[4 + j] = cvt_pk_bf16(mix_hi(q[2 * j], s24, mzs), mix_hi(q[2 * j + 1], s24, mzs));
   }
+}
+
+// CCQ without code cluster ("CCQ", section 3.5, "Dequantization without Code Cluster"): one
+// 64-weight group -> 32 dwords of bf16 pairs in k order.  The group's code bytes start at byte
+// 0 of c[0] (little endian); fin24 = super * 2^24, mzp24 = -zp / 2^24 (zp a power of two or 0,
+// so -zp * s is exact).  s = fl(s_q * super) is formed as fl(s_q * fin24) = s * 2^24 exactly.
+//
+// (4,3,2): byte b (< 21) holds weights 3b, 3b+1, 3b+2 as its states at shifts 4, 2, 0; byte 21
+// holds weight 63 in its high nibble and s_q in its low nibble.  Packed 16-bit shifts decode
+// bytes 4d, 4d+2 (even halves) and 4d+1, 4d+3 (odd halves) of each dword together.
+__device__ __forceinline__ void ccq432_decode64(const uint32_t (&c)[6], float fin24, float mzp24,
+                                                uint32_t (&p)[32]) {
+  const float s24 = (float)((c[5] >> 8) & 0xFu) * fin24;
+  const float mzs = s24 * mzp24;
+  float v[66];
+#pragma unroll
+  for (int d = 0; d < 6; ++d) {
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      const uint32_t x = odd ? ((c[d] >> 8) & 0x00FF00FFu) : (c[d] & 0x00FF00FFu);
+      const int b = 4 * d + odd;  // byte in the low half; b + 2 in the high half
+      const uint32_t q0 = pk_shr16(x, 4);  // x < 256 per half: no bits above the state
+      const uint32_t q1 = pk_shr16(x, 2) & 0x000F000Fu;
+      const uint32_t q2 = x & 0x000F000Fu;
+      if (3 * b < 64) v[3 * b] = mix_lo(q0, s24, mzs);
+      if (3 * b + 1 < 64) v[3 * b + 1] = mix_lo(q1, s24, mzs);
+      if (3 * b + 2 < 64) v[3 * b + 2] = mix_lo(q2, s24, mzs);
+      if (3 * b + 6 < 64) v[3 * b + 6] = mix_hi(q0, s24, mzs);
+      if (3 * b + 7 < 64) v[3 * b + 7] = mix_hi(q1, s24, mzs);
+      if (3 * b + 8 < 64) v[3 * b + 8] = mix_hi(q2, s24, mzs);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) p[i] = cvt_pk_bf16(v[2 * i], v[2 * i + 1]);
+}
+
+// Hybrid (3,3,2)+(3,4,2): u16 word j (< 9) holds weights 7j .. 7j+6 as its states at shifts
+// 13, 11, 9, 6, 4, 2, 0; word 9 holds weight 63 at shift 13 and s_q in bits 0..12.  Dword d
+// holds words 2d (low half) and 2d+1 (high half): one packed shift decodes a state of both.
+__device__ __forceinline__ void ccqh_decode64(const uint32_t (&c)[5], float fin24, float mzp24,
+                                              uint32_t (&p)[32]) {
+  const float s24 = (float)((c[4] >> 16) & 0x1FFFu) * fin24;
+  const float mzs = s24 * mzp24;
+  constexpr uint16_t sh[7] = {13, 11, 9, 6, 4, 2, 0};
+  float v[70];
+#pragma unroll
+  for (int d = 0; d < 5; ++d) {
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const uint32_t q = j == 0 ? pk_shr16(c[d], 13) : (pk_shr16(c[d], sh[j]) & 0x00070007u);
+      const int w = 14 * d + j;
+      if (w < 64) v[w] = mix_lo(q, s24, mzs);
+      if (w + 7 < 64) v[w + 7] = mix_hi(q, s24, mzs);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) p[i] = cvt_pk_bf16(v[2 * i], v[2 * i + 1]);
 }
 
 // ---------------------------------------------------------------------------------------------

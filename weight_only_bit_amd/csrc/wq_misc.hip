@@ -60,6 +60,43 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DevWeight w, int64_t
                    cvt_pk_bf16(v[14], v[15])};
 }
 
+// CCQ without code cluster ("CCQ", section 3.5, "Dequantization without Code Cluster", with the
+// (4,3,2) and (3,3,2)(3,4,2) rows of the configuration table): one thread per 16 weights of a
+// group; each weight is read from its own code word,
+//   s = f32(W[P-1] & s_mask) * super;  u = (W[i / p] >> shift[i % p]) & w_mask;
+//   x_hat = bf16(f32(u - zp) * s).
+template <int FMT>
+__global__ __launch_bounds__(256) void dequant_alg2_kernel(const DevWeight w, int64_t rows,
+                                                           uint16_t* __restrict__ out) {
+  constexpr bool HYB = FMT == FMT_CCQH;
+  constexpr int P = HYB ? 10 : 22, PW = HYB ? 7 : 3, GB = alg2_group_bytes(FMT);
+  constexpr uint32_t WMASK = HYB ? 0x7u : 0xFu, SMASK = HYB ? 0x1FFFu : 0xFu;
+  const int64_t quarters = w.k / 16;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * quarters) return;
+  const int64_t row = idx / quarters;
+  const int64_t k0 = (idx % quarters) * 16;
+  const int64_t g = k0 >> 6;
+  const uint8_t* grp = w.codes + row * (w.k / 64) * GB + g * GB;
+  auto word = [&](int j) -> uint32_t {
+    return HYB ? (uint32_t)grp[2 * j] | ((uint32_t)grp[2 * j + 1] << 8) : (uint32_t)grp[j];
+  };
+  const float s = (float)(word(P - 1) & SMASK) * w.super_scale[row];
+  float v[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int i = (int)(k0 & 63) + t;
+    const int j = i % PW;  // state within the word: shifts 13,11,9,6,4,2,0 or 4,2,0
+    const int sh = HYB ? (j < 3 ? 13 - 2 * j : 12 - 2 * j) : 4 - 2 * j;
+    v[t] = ccq_value((word(i / PW) >> sh) & WMASK, w.zp, s);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(out + row * w.k + k0);
+  dst[0] = (u32x4){cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3]), cvt_pk_bf16(v[4], v[5]),
+                   cvt_pk_bf16(v[6], v[7])};
+  dst[1] = (u32x4){cvt_pk_bf16(v[8], v[9]), cvt_pk_bf16(v[10], v[11]), cvt_pk_bf16(v[12], v[13]),
+                   cvt_pk_bf16(v[14], v[15])};
+}
+
 // ---------------------------------------------------------------------------------------------
 // Routing: a stable counting sort of the pairs by expert, in one workgroup of T threads.
 // Thread t owns the contiguous pairs [t c, (t + 1) c) (c = ceil(npairs / T)) and a private row
@@ -197,6 +234,10 @@ hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t
     hipLaunchKernelGGL(dequant_kernel<FMT_INT4>, grid, dim3(256), 0, stream, w, rows, out);
   else if (fmt == FMT_AFFINE2)
     hipLaunchKernelGGL(dequant_kernel<FMT_AFFINE2>, grid, dim3(256), 0, stream, w, rows, out);
+  else if (fmt == FMT_CCQ432)
+    hipLaunchKernelGGL(dequant_alg2_kernel<FMT_CCQ432>, grid, dim3(256), 0, stream, w, rows, out);
+  else if (fmt == FMT_CCQH)
+    hipLaunchKernelGGL(dequant_alg2_kernel<FMT_CCQH>, grid, dim3(256), 0, stream, w, rows, out);
   else
     hipLaunchKernelGGL(dequant_kernel<FMT_CCQ2>, grid, dim3(256), 0, stream, w, rows, out);
   return hipGetLastError();

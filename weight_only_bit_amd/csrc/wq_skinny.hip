@@ -31,11 +31,12 @@ namespace wq {
 namespace {
 
 constexpr int KCT_BASE = 512;  // activation columns per LDS chunk (all K-parts together)
-constexpr int FMT_INT4PC = 4;  // INT4 with one scale per output channel (kernel variant)
+constexpr int FMT_INT4PC = 8;  // INT4 with one scale per output channel (kernel variant)
 
 __host__ __device__ constexpr bool is_int4(int f) { return f == FMT_INT4 || f == FMT_INT4PC; }
 
-// Weights one lane decodes per step: 16 bytes of codes.
+// Weights one lane decodes per step: 16 bytes of codes, or one group of the CCQ formats
+// without code cluster (22 or 20 bytes).
 template <int FMT>
 __host__ __device__ constexpr int lane_weights() { return is_int4(FMT) ? 32 : 64; }
 
@@ -51,6 +52,7 @@ struct Raw {
   u32x4 codes;
   uint32_t scale;  // CCQ: the byte holding the 4-bit group scale; INT4 g64 / affine: bf16 bits
   uint32_t zero;   // affine zero point
+  u32x2 extra;     // (4,3,2): code bytes 16..23 of the aligned window; hybrid: bytes 16..19
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -66,7 +68,8 @@ struct WaveW {
   int32_t row_codes;   // byte offset of this lane's row and 16-weight slice in codes
   int32_t row_scales;  // byte offset of this lane's row in scales / qscale
   int32_t row_zeros;
-  uint32_t qshift;     // CCQ: 0 or 4, the nibble of the scale byte that is this lane's group
+  uint32_t qshift;     // CCQ: 0 or 4, the nibble of the scale byte that is this lane's group;
+                       // (4,3,2): 0 or 16, the bit offset of the group in its first dword
   float cs, cz;        // CCQ code scale / code zero of this lane's row
   float fin;           // CCQ super scale / INT4 per-channel scale of this lane's row
 };
@@ -98,6 +101,18 @@ __device__ __forceinline__ WaveW<FMT> wave_weight(const DevWeight& w, int64_t e,
     v.row_scales = (int32_t)(row * G * 2 + (gb + kb) * 2);
     v.zeros = make_rsrc(w.zeros + e * n * G, n * G);
     v.row_zeros = (int32_t)(row * G + gb + kb);
+  } else if constexpr (is_alg2(FMT)) {
+    // A group is 22 (or 20) bytes: lane kb's group gb + 4 j + kb starts at an even byte.  Loads
+    // read the dword-aligned window that holds it (the resource starts at the expert's first
+    // dword and ends at the dword holding its last byte, so the window stays in that dword).
+    constexpr int GB = alg2_group_bytes(FMT);
+    const uint8_t* eb = w.codes + e * n * G * GB;
+    const int64_t lead = (int64_t)(reinterpret_cast<uintptr_t>(eb) & 3u);
+    v.codes = make_rsrc(eb - lead, (lead + n * G * GB + 3) & ~(int64_t)3);
+    const int64_t off = lead + row * G * GB + (int64_t)(gb + kb) * GB;
+    v.qshift = 8u * (uint32_t)(off & 3);
+    v.row_codes = (int32_t)(off & ~(int64_t)3);
+    v.fin = w.super_scale[e * n + row];
   } else {
     const int64_t qb = (G + 1) / 2;
     v.codes = make_rsrc(w.codes + e * n * (k / 4), n * (k / 4));
@@ -116,6 +131,17 @@ __device__ __forceinline__ WaveW<FMT> wave_weight(const DevWeight& w, int64_t e,
 // st is wave-uniform and goes in the scalar offset.
 template <int FMT>
 __device__ __forceinline__ void load_raw(Raw<FMT>& r, const WaveW<FMT>& v, int32_t st) {
+  if constexpr (is_alg2(FMT)) {  // a step advances 4 groups: 88 or 80 bytes, dword aligned
+    constexpr int STEP = 4 * alg2_group_bytes(FMT);
+    r.codes = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(v.codes, v.row_codes, st * STEP, 0));
+    if constexpr (FMT == FMT_CCQ432)
+      r.extra = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(v.codes, v.row_codes + 16, st * STEP, 0));
+    else
+      r.extra.x = __builtin_amdgcn_raw_buffer_load_b32(v.codes, v.row_codes + 16, st * STEP, 0);
+    return;
+  }
   r.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v.codes, v.row_codes, st * 64, 0));
   if constexpr (FMT == FMT_INT4) {
     r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 4, 0);
@@ -258,6 +284,38 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
       for (int j = 0; j < SPC; ++j) {
         if (c * KCW + j * SSK >= Kpp) break;
         const Raw<FMT>& rw = r[j];
+        // lane's A fragments: row t*16 + nl, columns kw*KCW + j*SSK + kb*WPL + 8h
+        const uint8_t* abase = &lds[buf][nl * PITCH + (kw * KCW + j * SSK + kb * WPL) * 2];
+        if constexpr (is_alg2(FMT)) {
+          uint32_t p[32];
+          if constexpr (FMT == FMT_CCQ432) {
+            // shift the window so that the group starts at byte 0
+            const uint32_t w6[6] = {rw.codes[0], rw.codes[1], rw.codes[2], rw.codes[3],
+                                    rw.extra.x, rw.extra.y};
+            uint32_t c[6];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) c[i] = __builtin_amdgcn_alignbit(w6[i + 1], w6[i], W.qshift);
+            c[5] = w6[5] >> W.qshift;
+            ccq432_decode64(c, fin24, mzp24, p);
+          } else {
+            const uint32_t c[5] = {rw.codes[0], rw.codes[1], rw.codes[2], rw.codes[3], rw.extra.x};
+            ccqh_decode64(c, fin24, mzp24, p);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 B0 = {p[8 * q], p[8 * q + 1], p[8 * q + 2], p[8 * q + 3]};
+            const u32x4 B1 = {p[8 * q + 4], p[8 * q + 5], p[8 * q + 6], p[8 * q + 7]};
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+              const u32x4 A0 = *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32);
+              const u32x4 A1 =
+                  *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32 + 16);
+              acc[t] = mfma16x16x32(A0, B0, acc[t]);
+              acc[t] = mfma16x16x32(A1, B1, acc[t]);
+            }
+          }
+          continue;
+        }
         // s24 = s * 2^24 (the decode helpers' scaled form), mzs = -z * s
         float s24 = 0.0f, mzs = 0.0f;
         if constexpr (FMT == FMT_CCQ2) {
@@ -274,8 +332,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
           s24 = s * kTwo24;
           mzs = -(float)(rw.zero & 0xFFu) * s;
         }
-        // lane's A fragments: row t*16 + nl, columns kw*KCW + j*SSK + kb*WPL + 8h
-        const uint8_t* abase = &lds[buf][nl * PITCH + (kw * KCW + j * SSK + kb * WPL) * 2];
         // 16 weights (two MFMAs) at a time
 #pragma unroll
         for (int q = 0; q < WPL / 16; ++q) {
@@ -433,6 +489,10 @@ hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const Skinn
       return launch_fmt<FMT_INT4>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
     case FMT_AFFINE2:
       return launch_fmt<FMT_AFFINE2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_CCQ432:
+      return launch_fmt<FMT_CCQ432>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_CCQH:
+      return launch_fmt<FMT_CCQH>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
     default: return launch_fmt<FMT_CCQ2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
   }
 }

@@ -594,7 +594,8 @@ hipError_t launch_mode(int fmt, const TiledArgs& a, int64_t row_tiles, hipStream
   switch (fmt) {
     case FMT_INT4: return launch_t<FMT_INT4, MODE>(a, row_tiles, s);
     case FMT_AFFINE2: return launch_t<FMT_AFFINE2, MODE>(a, row_tiles, s);
-    default: return launch_t<FMT_CCQ2, MODE>(a, row_tiles, s);
+    case FMT_CCQ2: return launch_t<FMT_CCQ2, MODE>(a, row_tiles, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
