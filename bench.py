@@ -53,6 +53,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# --wformat name -> (wq format id, zero point, label)
+WFORMATS = {"ccq": (3, 32, "CCQ (6,4,3) code cluster g64"),
+            "ccq432": (4, 8, "CCQ (4,3,2) g64"),
+            "ccqh": (5, 4, "CCQ hybrid (3,3,2)+(3,4,2) g64")}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,6 +69,10 @@ def parse():
     ap.add_argument("--tokens", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens per sampled layer for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wformat", default="ccq", choices=list(WFORMATS),
+                    help="2-bit-class format of the MoE layers (moe_stack_decode, moe_prefill): "
+                         "ccq = (6,4,3) code cluster, 2.06 bpw (default); ccq432 = (4,3,2), "
+                         "2.75 bpw; ccqh = hybrid (3,3,2)+(3,4,2), 2.5 bpw")
     ap.add_argument("--workload", default="moe_stack_decode",
                     choices=["moe_stack_decode", "moe_prefill", "dense_decode", "copy_calibration",
                              "pages_shapes"],
@@ -75,11 +85,12 @@ def parse():
 
 def make_layer(wq, synth, fmt, E, H, I, seed, group):
     """gate, up, down PackedWeight for one layer, drawn on the GPU."""
+    zp = {f: z for f, z, _ in WFORMATS.values()}.get(fmt, 32)
     ws = []
     for j, (n, k) in enumerate(((I, H), (I, H), (H, I))):
         arr = synth.random_packed_device(fmt, E, n, k, seed * 16 + j, group=group)
         ws.append(wq.PackedWeight(fmt, n, k, E, group, *(arr.get(f) for f in (
-            "codes", "scales", "zeros", "qscale", "super_scale", "code_scale", "code_zero")), 32))
+            "codes", "scales", "zeros", "qscale", "super_scale", "code_scale", "code_zero")), zp))
     return ws
 
 
@@ -134,7 +145,7 @@ def main():
     t0 = time.time()
     layers = []
     for l in range(L):
-        fmt, group = (wq.FMT_INT4, 0) if l < n4 else (wq.FMT_CCQ2, 64)
+        fmt, group = (wq.FMT_INT4, 0) if l < n4 else (WFORMATS[args.wformat][0], 64)
         layers.append(make_layer(wq, synth, fmt, E, H, I, 1000 + l, group))
         if l % 8 == 7 or l == L - 1:
             torch.cuda.synchronize()
@@ -236,7 +247,8 @@ def main():
         parity = max(errs)
 
     out = {
-        "metric": "weight-stream HBM GB/s (decode M<=32), w2/w4 MoE stack",
+        "metric": "weight-stream HBM GB/s (decode M<=32), w2/w4 MoE stack"
+                  + ("" if args.wformat == "ccq" else f" [{WFORMATS[args.wformat][2]}]"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -249,13 +261,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded random packed codes/scales, N(0,1) activations, uniform top-8 routing)",
         "config": {"workload": "moe_stack_decode", "layers": L, "int4_per_channel_layers": n4,
-                   "ccq_g64_layers": L - n4, "experts": E, "topk": K, "hidden": H, "inter": I,
+                   "ccq_g64_layers": L - n4, "ccq_format": WFORMATS[args.wformat][2], "experts": E, "topk": K, "hidden": H, "inter": I,
                    "tokens": T, "resident_weight_bytes": resident,
                    "step_weight_bytes": step_weight_bytes, "step_activation_bytes": step_act_bytes},
         "tokens_per_s": round(tok_s, 2),
-        "roofline": {"kernel": "skinny_kernel CCQ gate+up (MODE_GATEUP)", "bound": "hbm",
+        "roofline": {"kernel": f"skinny_kernel {WFORMATS[args.wformat][2]} gate+up (MODE_GATEUP)",
+                     "bound": "hbm",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if args.wformat == "ccq" else None,
                      "avg_launch_us": round(gu_avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(gu_bytes)},
         "cpu_baseline": cpu,
@@ -281,7 +294,7 @@ def moe_prefill(args):
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     E, H, I, K, T = 64, 8192, 3584, 8, 4096
-    g, u, dn = make_layer(wq, synth, wq.FMT_CCQ2, E, H, I, 2000, 64)
+    g, u, dn = make_layer(wq, synth, WFORMATS[args.wformat][0], E, H, I, 2000, 64)
     x = torch.from_numpy(synth.acts_bf16((T, H), 501).view(np.int16)).to(dev)
     ids, wts = synth.routing_zipf(T, K, E, 601)
     ids_d, wts_d = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
@@ -329,17 +342,20 @@ def moe_prefill(args):
     log(f"layer {ms * 1e3:.0f} us ({tf:.1f} TFLOP/s); stages: " +
         ", ".join(f"{k} {v:.0f} us" for k, v in stage_us.items()) +
         f"; gate+up {gu_tf:.1f} TFLOP/s, down {dn_tf:.1f} TFLOP/s")
-    out = {"metric": "bf16 TFLOP/s (prefill MoE layer, CCQ g64)", "value": round(tf, 2),
+    out = {"metric": f"bf16 TFLOP/s (prefill MoE layer, {WFORMATS[args.wformat][2]})",
+           "value": round(tf, 2),
            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "moe_prefill", "tokens": T, "topk": K, "experts": E,
                       "hidden": H, "inter": I, "routing": "zipf s=1.1",
+                      "format": WFORMATS[args.wformat][2],
                       "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())},
            "tokens_per_s": round(T / (ms * 1e-3), 1),
            "stage_us": {k: round(v, 1) for k, v in stage_us.items()},
            "down_tflops": round(dn_tf, 2),
-           "roofline": {"kernel": "tiled_kernel CCQ gate+up (MODE_GATEUP)", "bound": "mfma",
+           "roofline": {"kernel": f"tiled_kernel {WFORMATS[args.wformat][2]} gate+up (MODE_GATEUP)",
+                        "bound": "mfma",
                         "achieved": round(gu_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": None, "avg_launch_us": round(stage_us["gate_up"], 1),

@@ -342,7 +342,7 @@ def test_tiled_gemm_decodes_every_weight_bit_exact(wq):
             assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + w])), f"{name} columns {c0}.."
 
 
-@pytest.mark.parametrize("name", ["ccq", "int4pc"])
+@pytest.mark.parametrize("name", ["ccq", "int4pc", "ccq432", "ccqh"])
 def test_moe_prefill_skewed_routing(wq, name):
     # Zipf-biased routing as in the prefill workload, at reduced sizes: most rows go to the
     # first experts (several 128-row tiles), the tail experts get a few rows or none.

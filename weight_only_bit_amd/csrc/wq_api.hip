@@ -33,9 +33,11 @@ wq_status hip_status(hipError_t e, const char* what) {
   return fail(WQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Formats the tiled (many-row) kernels implement; the others run the decode-streaming kernels
-// for every row count.
-bool has_tiled(int32_t f) { return f == WQ_FMT_INT4 || f == WQ_FMT_INT2_AFFINE || f == WQ_FMT_CCQ2; }
+// Formats the tiled (many-row) kernels implement (all of them).
+bool has_tiled(int32_t f) {
+  return f == WQ_FMT_INT4 || f == WQ_FMT_INT2_AFFINE || f == WQ_FMT_CCQ2 || f == WQ_FMT_CCQ432 ||
+         f == WQ_FMT_CCQ_HYBRID;
+}
 
 bool is_ccq(int32_t f) {
   return f == WQ_FMT_CCQ2 || f == WQ_FMT_CCQ432 || f == WQ_FMT_CCQ_HYBRID;

@@ -26,6 +26,12 @@
 //     step is read right after the step's barrier, under the last slice's MFMAs.
 // Waves of a ragged tile still run every MFMA (rows past the end read the tile's first row);
 // their results are not stored.
+//
+// The CCQ formats without code cluster ((4,3,2) and the hybrid) keep a group's scale in its last
+// code word, so a group cannot be split between lanes cheaply.  There lane l copies and decodes
+// the whole group of wave row l (64 weights), and v_permlane32_swap hands each lane half the
+// other half's k-range: after the swap lane (n, h) holds k = 32 h .. 32 h + 31 of rows n and
+// 32 + n, the same fragments as above.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -60,12 +66,14 @@ __device__ __forceinline__ uint8_t* a_stage() {
 #define WQ_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
 
-// Packed bytes one lane decodes per step for one weight row: 32 weights.
+// Packed bytes one lane decodes per step for one weight row: 32 weights (the CCQ formats
+// without code cluster: the 64 weights of one row).
 template <int FMT>
 struct Codes {
-  u32x4 c;         // 2-bit formats: c.x, c.y (8 bytes); INT4: all 16 bytes
+  u32x4 c;         // 2-bit formats: c.x, c.y (8 bytes); INT4 and (4,3,2) / hybrid: 16 bytes
   uint32_t scale;  // CCQ: scale byte; INT4 / affine: bf16 bits
   uint32_t zero;   // affine zero point
+  u32x2 t;         // (4,3,2): bytes 16..23 of the aligned window; hybrid: bytes 16..19
 };
 
 // Where one weight row's packed data lives; the row is copied to LDS by one lane of its wave.
@@ -95,6 +103,8 @@ __device__ __forceinline__ RowSrc row_src(const DevWeight& w, int64_t e, int64_t
     r.scale = reinterpret_cast<const uint8_t*>(w.scales + grow * G);
     r.zeros = w.zeros + grow * G;
     r.gstep = 2;
+  } else if (is_alg2(FMT)) {
+    r.codes = w.codes + grow * G * alg2_group_bytes(FMT);
   } else {
     r.codes = w.codes + grow * (k / 4);
     r.scale = w.qscale + grow * ((G + 1) / 2);
@@ -135,16 +145,20 @@ __device__ __forceinline__ void cdecode(const Codes<FMT>& p, const RowConst& r, 
 }
 
 // Packed-data LDS ring, per wave and stage: codes (64 rows x 16 bytes, INT4: two such halves),
-// then one dword per row for the scale, then (affine) one for the zero point.
+// then one dword per row for the scale, then (affine) one for the zero point.  (4,3,2) and
+// hybrid: the first 16 bytes of each row's group window, then one (hybrid) or two ((4,3,2))
+// dwords per row for the rest.
 template <int FMT>
 struct CodeRing {
   static constexpr int CODE_BYTES = (FMT == FMT_INT4 ? 2 : 1) * 64 * 16;
-  static constexpr int WAVE_BYTES = CODE_BYTES + 256 * (FMT == FMT_AFFINE2 ? 2 : 1);
+  static constexpr int WAVE_BYTES =
+      CODE_BYTES + 256 * ((FMT == FMT_AFFINE2 || FMT == FMT_CCQ432) ? 2 : 1);
   static constexpr int STAGE_BYTES = 4 * WAVE_BYTES;
   static constexpr int DEPTH = (FMT == FMT_INT4) ? 2 : 4;  // stages (fits 160 KB with A)
   static constexpr int AHEAD = DEPTH - 1 > 2 ? DEPTH - 1 : 2;  // steps between copy and decode
-  // memory instructions per step per lane: codes, scale, zero
-  static constexpr int VMEM = (FMT == FMT_INT4 ? 2 : 1) + 1 + (FMT == FMT_AFFINE2 ? 1 : 0);
+  // memory instructions per step per lane: codes, scale, zero / window pieces
+  static constexpr int VMEM = is_alg2(FMT) ? (FMT == FMT_CCQ432 ? 3 : 2)
+                                           : (FMT == FMT_INT4 ? 2 : 1) + 1 + (FMT == FMT_AFFINE2 ? 1 : 0);
 };
 
 // Row tiles.  An expert's (or the dense matrix's) rows are covered by full 256-row tiles; the
@@ -204,12 +218,14 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   }
   const float mzp24 = -(float)args.w0.zp / kTwo24;
   RowSrc rs;
+  float own_fin24 = 0.f;  // (4,3,2) / hybrid: super scale * 2^24 of wave row `lane`
   {
     const int jj = lane >> 5;  // wave row `lane` = 32 jj + (lane % 32)
     const int64_t r = (MODE == MODE_GATEUP) ? n0 + 32 * wave + (lane & 31)
                                             : n0 + 64 * wave + lane;
     const DevWeight& w = (MODE == MODE_GATEUP && jj == 1) ? args.w1 : args.w0;
     rs = row_src<FMT>(w, e, r < N ? r : N - 1);
+    if constexpr (is_alg2(FMT)) own_fin24 = w.super_scale[e * w.n + (r < N ? r : N - 1)] * kTwo24;
   }
 
   // ---- activation copy role ----
@@ -276,6 +292,21 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   };
   auto copy_codes = [&](int64_t g, auto stc) __attribute__((always_inline)) {
     uint8_t* base = c_stage(stc);
+    if constexpr (is_alg2(FMT)) {
+      // the dword-aligned window holding group g (a (4,3,2) group may start 2 bytes into a
+      // dword; its window's last dword then holds the group's last 2 bytes)
+      const uint8_t* p = rs.codes + g * alg2_group_bytes(FMT);
+      if constexpr (FMT == FMT_CCQ432)
+        p = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)3);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(p),
+                                       (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(p + 16),
+                                       (__attribute__((address_space(3))) void*)(base + 1024), 4, 0, 0);
+      if constexpr (FMT == FMT_CCQ432)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(p + 20),
+                                         (__attribute__((address_space(3))) void*)(base + 1280), 4, 0, 0);
+      return;
+    }
     if constexpr (FMT == FMT_INT4) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.codes + g * 32),
                                        (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
@@ -306,6 +337,36 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   // share a register with an address.
   auto read_codes = [&](Codes<FMT>(&cc)[2], auto stc) __attribute__((always_inline)) {
     const uint8_t* base = c_stage(stc);
+    if constexpr (is_alg2(FMT)) {  // the lane's own row: 16 + 4 (+ 4) bytes
+      const uint32_t oa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
+          base + lane * 16);
+      const uint32_t ta = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
+          base + 1024 + lane * 4);
+      u32x4 c0;
+      uint32_t t0, t1;
+      if constexpr (FMT == FMT_CCQ432) {
+        asm volatile(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b32 %1, %4\n\t"
+            "ds_read_b32 %2, %4 offset:256\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(c0), "=&v"(t0), "=&v"(t1)
+            : "v"(oa), "v"(ta)
+            : "memory");
+      } else {
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b32 %1, %3\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(c0), "=&v"(t0)
+            : "v"(oa), "v"(ta)
+            : "memory");
+        t1 = 0u;
+      }
+      cc[0].c = c0;
+      cc[0].t = (u32x2){t0, t1};
+      return;
+    }
     const uint32_t ca = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
         base + (FMT == FMT_INT4 ? kh * 1024 + l32 * 16 : l32 * 16 + kh * 8));
     const uint32_t sa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
@@ -365,11 +426,42 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
     }
   };
   auto clamp_step = [&](int64_t g) __attribute__((always_inline)) { return g < last ? g : last; };
+  // (4,3,2) / hybrid: decode the lane's whole group, then swap lane halves so that lane
+  // (n, h) holds k = 32 h .. 32 h + 31 of wave rows n (j = 0) and 32 + n (j = 1).
+  auto decode_rows = [&](const Codes<FMT>(&cc)[2], int64_t g, uint32_t(&dst)[2][16])
+      __attribute__((always_inline)) {
+    if constexpr (is_alg2(FMT)) {
+      uint32_t p[32];
+      if constexpr (FMT == FMT_CCQ432) {
+        const uint32_t sh =
+            8u * (((uint32_t)reinterpret_cast<uintptr_t>(rs.codes) + 22u * (uint32_t)g) & 3u);
+        const uint32_t w6[6] = {cc[0].c.x, cc[0].c.y, cc[0].c.z, cc[0].c.w, cc[0].t.x, cc[0].t.y};
+        uint32_t c[6];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) c[i] = __builtin_amdgcn_alignbit(w6[i + 1], w6[i], sh);
+        c[5] = w6[5] >> sh;
+        ccq432_decode64(c, own_fin24, mzp24, p);
+      } else {
+        const uint32_t c[5] = {cc[0].c.x, cc[0].c.y, cc[0].c.z, cc[0].c.w, cc[0].t.x};
+        ccqh_decode64(c, own_fin24, mzp24, p);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // lower lanes keep p[i] and receive the upper lane's p[i]; upper lanes keep p[16 + i]
+        // and receive the lower lane's p[16 + i]
+        const auto r = __builtin_amdgcn_permlane32_swap(p[i], p[16 + i], false, false);
+        dst[0][i] = r[0];
+        dst[1][i] = r[1];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) cdecode<FMT>(cc[j], rc[j], g, mzp24, dst[j]);
+    }
+  };
   auto decode_step = [&](int64_t g, auto cstc, uint32_t(&dst)[2][16]) __attribute__((always_inline)) {
     Codes<FMT> cc[2];
     read_codes(cc, cstc);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) cdecode<FMT>(cc[j], rc[j], g, mzp24, dst[j]);
+    decode_rows(cc, g, dst);
   };
   // Memory instructions issued per iteration: packed data, then the 8 activation copies.
   constexpr int VMEM_PER_ITER = Ring::VMEM + MT;
@@ -408,8 +500,7 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
     read_a(X, 2, stc);
     mma(Y, Bw[PB], 1);
     read_a(Y, 3, stc);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) cdecode<FMT>(cc[j], rc[j], clamp_step(g + 1), mzp24, Bw[PB ^ 1][j]);
+    decode_rows(cc, clamp_step(g + 1), Bw[PB ^ 1]);
     mma(X, Bw[PB], 2);
     // 0x100 LDS read, 0x8 MFMA, 0x2 VALU
     __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
@@ -595,6 +686,8 @@ hipError_t launch_mode(int fmt, const TiledArgs& a, int64_t row_tiles, hipStream
     case FMT_INT4: return launch_t<FMT_INT4, MODE>(a, row_tiles, s);
     case FMT_AFFINE2: return launch_t<FMT_AFFINE2, MODE>(a, row_tiles, s);
     case FMT_CCQ2: return launch_t<FMT_CCQ2, MODE>(a, row_tiles, s);
+    case FMT_CCQ432: return launch_t<FMT_CCQ432, MODE>(a, row_tiles, s);
+    case FMT_CCQH: return launch_t<FMT_CCQH, MODE>(a, row_tiles, s);
     default: return hipErrorInvalidValue;
   }
 }
