@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-INT4, AFFINE2, CCQ, CCQ432, CCQ_HYBRID = 1, 2, 3, 4, 5
+INT4, AFFINE2, CCQ, CCQ432, CCQ_HYBRID, INT8 = 1, 2, 3, 4, 5, 6
 CCQ_ZP = 32  # reading: weight zero point 2^(L-1) for L = 6
 CCQ432_ZP = 8  # reading: 2^(L-1) for the 4-bit states of (4,3,2)
 CCQ_HYBRID_ZP = 4  # reading: 2^(L-1) for the 3-bit states of (3,3,2)(3,4,2)
@@ -101,6 +101,7 @@ def lib():
             "orc_ccq_search": (ctypes.c_uint32, [vp, ctypes.c_double, i32, vp]),
             "orc_quant_ccq": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
             "orc_quant_alg2": (i32, [vp, i64, i64, i32, i32, i32, vp, vp]),
+            "orc_quant_int8": (i32, [vp, i64, i64, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -303,6 +304,14 @@ def quantize(w, fmt: int, group: int = 64, refine: bool = True, zp: int | None =
         if rc:
             raise ValueError("bad INT4 shape/group")
         return Packed(INT4, n, k, E, group, codes.reshape(E, n, -1),
+                      scales.reshape(E, n, -1) if group else scales.reshape(E, n))
+    if fmt == INT8:
+        codes = np.zeros((E * n, k), np.int8)
+        scales = np.zeros((E * n, G if group else 1), np.uint16)
+        rc = lib().orc_quant_int8(_p(flat), E * n, k, group, _p(codes), _p(scales))
+        if rc:
+            raise ValueError("bad INT8 shape/group")
+        return Packed(INT8, n, k, E, group, codes.view(np.uint8).reshape(E, n, k),
                       scales.reshape(E, n, -1) if group else scales.reshape(E, n))
     if fmt == AFFINE2:
         codes = np.zeros((E * n, k // 4), np.uint8)

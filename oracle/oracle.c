@@ -183,6 +183,8 @@ ORC_API double orc_ccq_bpw(int32_t T, int32_t g, int32_t N, int32_t scale_bits) 
 /*   format 5: CCQ hybrid (3,3,2)+(3,4,2), 2.5 bpw: 10 u16 code words per group (little      */
 /*             endian), codes u8[E][n][k/64*20]; the last word's low 13 bits hold the group's */
 /*             quantized scale; super f32 [E][n], zp.                                         */
+/*   format 6: WINT8, one signed byte per weight (two's complement), codes i8[E][n][k];       */
+/*             scales bf16 [E][n][k/64] (group 64) or [E][n] (group 0, per output channel).   */
 /* ------------------------------------------------------------------------------------------ */
 
 typedef struct {
@@ -201,7 +203,7 @@ typedef struct {
   int32_t zp;
 } orc_weight;
 
-enum { ORC_INT4 = 1, ORC_AFFINE2 = 2, ORC_CCQ = 3, ORC_CCQ432 = 4, ORC_CCQ_HYBRID = 5 };
+enum { ORC_INT4 = 1, ORC_AFFINE2 = 2, ORC_CCQ = 3, ORC_CCQ432 = 4, ORC_CCQ_HYBRID = 5, ORC_INT8 = 6 };
 
 /* [E6.4] "Do it in code" (sign-extended 4-bit field) and "Math and notation" (x_hat = s(q-z)
  * with z = 0): W_hat = bf16(f32(q) * f32(s)). */
@@ -210,6 +212,18 @@ static uint16_t decode_int4(const orc_weight* w, int64_t e, int64_t n, int64_t k
   uint8_t byte = w->codes[row * (w->k / 2) + (k >> 1)];
   int32_t nib = (byte >> (4 * (k & 1))) & 0xF;
   int32_t q = nib >= 8 ? nib - 16 : nib;
+  float s = (w->group == 0) ? bf16_to_f32(w->scales[row])
+                            : bf16_to_f32(w->scales[row * (w->k / w->group) + k / w->group]);
+  float d = (float)q * s;
+  return f32_to_bf16(d);
+}
+
+/* WINT8 (FastDeploy "Quantization" precision list: INT8 weights, BF16 activations) read with the
+ * [E6.4] formula x_hat = s(q - z), z = 0, at b = 8: W_hat = bf16(f32(q) * f32(s)), q the byte as
+ * a signed 8-bit integer.  Reading: the scale granularity follows INT4 (group 64 or per channel). */
+static uint16_t decode_int8(const orc_weight* w, int64_t e, int64_t n, int64_t k) {
+  int64_t row = e * w->n + n;
+  int32_t q = (int32_t)(int8_t)w->codes[row * w->k + k];
   float s = (w->group == 0) ? bf16_to_f32(w->scales[row])
                             : bf16_to_f32(w->scales[row * (w->k / w->group) + k / w->group]);
   float d = (float)q * s;
@@ -303,6 +317,7 @@ static uint16_t decode_alg2(const orc_weight* w, int64_t e, int64_t n, int64_t k
 static uint16_t decode_one(const orc_weight* w, int64_t e, int64_t n, int64_t k) {
   switch (w->format) {
     case ORC_INT4: return decode_int4(w, e, n, k);
+    case ORC_INT8: return decode_int8(w, e, n, k);
     case ORC_AFFINE2: return decode_affine2(w, e, n, k);
     case ORC_CCQ432:
     case ORC_CCQ_HYBRID: return decode_alg2(w, e, n, k);
@@ -312,7 +327,7 @@ static uint16_t decode_one(const orc_weight* w, int64_t e, int64_t n, int64_t k)
 
 static int check_weight(const orc_weight* w) {
   if (w->k <= 0 || w->n <= 0 || w->k % 64 != 0) return -1;
-  if (w->format == ORC_INT4) return (w->group == 64 || w->group == 0) ? 0 : -1;
+  if (w->format == ORC_INT4 || w->format == ORC_INT8) return (w->group == 64 || w->group == 0) ? 0 : -1;
   if (w->format == ORC_AFFINE2 || w->format == ORC_CCQ || w->format == ORC_CCQ432 ||
       w->format == ORC_CCQ_HYBRID)
     return w->group == 64 ? 0 : -1;
@@ -498,6 +513,38 @@ ORC_API int32_t orc_quant_int4(const float* w, int64_t n, int64_t k, int32_t gro
           *b = (uint8_t)(q & 0xF);
         else
           *b = (uint8_t)(*b | ((q & 0xF) << 4));
+      }
+    }
+  }
+  return 0;
+}
+
+/* WINT8 round-to-nearest: s = bf16(absmax / 127) per group of 64 (or per row for group 0),
+ * q = clip(round_half_even(w / s), -128, 127) (the [E6.4] affine quantizer with z = 0 at b = 8);
+ * a zero group gets q = 0. */
+ORC_API int32_t orc_quant_int8(const float* w, int64_t n, int64_t k, int32_t group,
+                               int8_t* codes, uint16_t* scales) {
+  if (k % 64 || (group != 64 && group != 0)) return -1;
+  int64_t gsz = group ? group : k;
+  int64_t groups = k / gsz;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t g = 0; g < groups; ++g) {
+      const float* src = w + r * k + g * gsz;
+      float amax = 0.0f;
+      for (int64_t i = 0; i < gsz; ++i) amax = fmaxf(amax, fabsf(src[i]));
+      uint16_t sb = f32_to_bf16(amax / 127.0f);
+      scales[r * groups + g] = sb;
+      float s = bf16_to_f32(sb);
+      for (int64_t i = 0; i < gsz; ++i) {
+        int32_t q = 0;
+        if (s != 0.0f) {
+          float v = nearbyintf(src[i] / s);
+          if (v < -128.0f) v = -128.0f;
+          if (v > 127.0f) v = 127.0f;
+          q = (int32_t)v;
+        }
+        codes[r * k + g * gsz + i] = (int8_t)q;
       }
     }
   }
