@@ -35,6 +35,10 @@
  *                           s_mask 0xF.  Hybrid: u16 words, P = 10, p = 7, shifts
  *                           13,11,9,6,4,2,0, w_mask 0x7, s_mask 0x1FFF.  The last word carries
  *                           weight 63 in its top state and the group scale in its low bits.
+ *       WQ_FMT_INT8         WINT8: one signed byte per weight (two's complement); x_hat = s * q
+ *                           with a bf16 scale per group of 64 along k or per output channel
+ *                           (group = 0) (FastDeploy "Quantization" precision list: INT8 weights,
+ *                           BF16 activations; lesson E6.4 "Math and notation" at b = 8).
  *
  * Layouts (every matrix is W[n][k], k contiguous, y = x W^T; an MoE tensor adds a leading
  * expert dimension; group = 64 along k; G = k / 64):
@@ -47,6 +51,7 @@
  *           super_scale f32[E][n]; zp (8 for the 4-bit states).
  *   CCQ_HYBRID: codes u8[E][n][G*20] (each group's 10 u16 words, little endian);
  *           super_scale f32[E][n]; zp (4 for the 3-bit states).
+ *   INT8:   codes i8[E][n][k]; scales bf16[E][n][G] (group 64) or bf16[E][n] (group 0).
  *
  * Conventions for every call below:
  *   - Every pointer inside wq_weight and every tensor argument of a compute call is DEVICE
@@ -93,18 +98,19 @@ typedef enum {
   WQ_FMT_INT2_AFFINE = 2,
   WQ_FMT_CCQ2 = 3,
   WQ_FMT_CCQ432 = 4,
-  WQ_FMT_CCQ_HYBRID = 5
+  WQ_FMT_CCQ_HYBRID = 5,
+  WQ_FMT_INT8 = 6
 } wq_format;
 
 /* A packed weight tensor [experts][n][k] in device memory (see layouts above). */
 typedef struct {
   int32_t format;            /* wq_format                                                  */
-  int32_t group;             /* 64, or 0 = per output channel (INT4 only)                  */
+  int32_t group;             /* 64, or 0 = per output channel (INT4 and INT8)              */
   int64_t experts;           /* 1 for a dense matrix                                       */
   int64_t n;                 /* output channels per expert                                 */
   int64_t k;                 /* input channels; a multiple of 64                           */
   const uint8_t* codes;
-  const uint16_t* scales;    /* bf16 bits; INT4 and AFFINE                                 */
+  const uint16_t* scales;    /* bf16 bits; INT4, INT8 and AFFINE                           */
   const uint8_t* zeros;      /* AFFINE                                                     */
   const uint8_t* qscale;     /* CCQ2                                                       */
   const float* super_scale;  /* CCQ2, CCQ432, CCQ_HYBRID                                   */

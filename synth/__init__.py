@@ -15,7 +15,7 @@ import numpy as np
 
 SEED = 20261203
 
-FMT_INT4, FMT_AFFINE2, FMT_CCQ, FMT_CCQ432, FMT_CCQ_HYBRID = 1, 2, 3, 4, 5
+FMT_INT4, FMT_AFFINE2, FMT_CCQ, FMT_CCQ432, FMT_CCQ_HYBRID, FMT_INT8 = 1, 2, 3, 4, 5, 6
 _GROUP_BYTES = {FMT_CCQ432: 22, FMT_CCQ_HYBRID: 20}
 # super scale that puts a uniform group-scale field at the magnitude of a N(0, 0.02) group:
 # absmax ~ 3 std over (2^(L-1) - 1) levels, spread over the field's range
@@ -81,6 +81,9 @@ def packed_layout(fmt: int, experts: int, n: int, k: int, group: int = 64) -> di
     if fmt == FMT_INT4:
         return {"codes": ((experts, n, k // 2), np.uint8),
                 "scales": ((experts, n, G) if group else (experts, n), np.uint16)}
+    if fmt == FMT_INT8:
+        return {"codes": ((experts, n, k), np.uint8),
+                "scales": ((experts, n, G) if group else (experts, n), np.uint16)}
     if fmt == FMT_AFFINE2:
         return {"codes": ((experts, n, k // 4), np.uint8),
                 "scales": ((experts, n, G), np.uint16),
@@ -99,7 +102,7 @@ def packed_layout(fmt: int, experts: int, n: int, k: int, group: int = 64) -> di
 
 def random_packed(fmt: int, experts: int, n: int, k: int, *path: int, group: int = 64) -> dict:
     """Random packed weights on the host: uniform code bytes; scales of the magnitude a
-    N(0, 0.02) weight would get (INT4 ~ 0.02*U(2,3)/7, affine ~ 0.02*U(3,5)/3 with zero
+    N(0, 0.02) weight would get (INT4 ~ 0.02*U(2,3)/7, INT8 ~ 0.02*U(2,3)/127, affine ~ 0.02*U(3,5)/3 with zero
     points in 0..3); CCQ group scales uniform in 1..15, super scale 0.02*3/31/15, code scale
     U(64, 128) and an integral code zero that keeps 255*scale + zero below 2^15.  The CCQ
     formats without code cluster draw every code byte (scale fields included) uniformly, with
@@ -110,6 +113,8 @@ def random_packed(fmt: int, experts: int, n: int, k: int, *path: int, group: int
     out["codes"] = g.integers(0, 256, size=lay["codes"][0], dtype=np.uint8)
     if fmt == FMT_INT4:
         out["scales"] = bf16_bits(0.02 * g.uniform(2.0, 3.0, size=lay["scales"][0]) / 7.0)
+    elif fmt == FMT_INT8:
+        out["scales"] = bf16_bits(0.02 * g.uniform(2.0, 3.0, size=lay["scales"][0]) / 127.0)
     elif fmt == FMT_AFFINE2:
         out["scales"] = bf16_bits(0.02 * g.uniform(3.0, 5.0, size=lay["scales"][0]) / 3.0)
         out["zeros"] = g.integers(0, 4, size=lay["zeros"][0], dtype=np.uint8)
@@ -147,6 +152,8 @@ def random_packed_device(fmt: int, experts: int, n: int, k: int, seed: int, devi
                                   generator=gen)}
     if fmt == FMT_INT4:
         out["scales"] = (0.02 * u(lay["scales"][0], 2.0, 3.0) / 7.0).to(torch.bfloat16).view(torch.int16)
+    elif fmt == FMT_INT8:
+        out["scales"] = (0.02 * u(lay["scales"][0], 2.0, 3.0) / 127.0).to(torch.bfloat16).view(torch.int16)
     elif fmt == FMT_AFFINE2:
         out["scales"] = (0.02 * u(lay["scales"][0], 3.0, 5.0) / 3.0).to(torch.bfloat16).view(torch.int16)
         out["zeros"] = torch.randint(0, 4, lay["zeros"][0], dtype=torch.uint8, device=device,

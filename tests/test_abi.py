@@ -93,7 +93,9 @@ def _weight(wq, **kw):
     (dict(format=5, super_scale=0x3004), -3),  # misaligned super scale
     (dict(format=5, zp=6), -2),               # hybrid zero point not a power of two
     (dict(format=4, group=0), -2),
-    (dict(format=6), -2),
+    (dict(format=6, scales=None), -1),        # INT8 needs scales
+    (dict(format=6, group=32, scales=0x6000), -2),
+    (dict(format=7), -2),
 ])
 def test_gemm_rejects_bad_descriptors_without_launch(wq, kw, status):
     L = wq.lib()

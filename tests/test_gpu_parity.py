@@ -17,8 +17,15 @@ from wq_testutil import assert_close, to_device, torch_bf16_bits
 pytestmark = pytest.mark.gpu
 
 FMTS = {"int4": oracle.INT4, "affine2": oracle.AFFINE2, "ccq": oracle.CCQ,
-        "ccq432": oracle.CCQ432, "ccqh": oracle.CCQ_HYBRID}
-ALL = ["int4", "int4pc", "affine2", "ccq", "ccq432", "ccqh"]
+        "ccq432": oracle.CCQ432, "ccqh": oracle.CCQ_HYBRID, "int8": oracle.INT8}
+ALL = ["int4", "int4pc", "affine2", "ccq", "ccq432", "ccqh", "int8", "int8pc"]
+
+
+def _fmt_group(name):
+    """Format id and group of a test name (the "pc" names are per-channel INT4 / INT8)."""
+    if name.endswith("pc"):
+        return FMTS[name[:-2]], 0
+    return FMTS[name], 64
 
 
 def _say(*a):
@@ -65,8 +72,7 @@ def _random_packed(fmt, E, n, k, seed, group=64):
 @pytest.mark.parametrize("name", ALL)
 @pytest.mark.parametrize("src", ["quantized", "random"])
 def test_dequantize_bit_exact(wq, name, src):
-    fmt = FMTS["int4" if name == "int4pc" else name]
-    group = 0 if name == "int4pc" else 64
+    fmt, group = _fmt_group(name)
     E, n, k = 2, 40, 320  # 5 groups: an odd count exercises the half-used qscale byte
     _say(f"dequant {name} {src} E={E} n={n} k={k}")
     if src == "quantized":
@@ -142,8 +148,7 @@ DENSE_SHAPES = [(80, 576), (128, 1024), (512, 512)]
 def test_gemm_parity(wq, name, nk, m):
     import torch
 
-    fmt = FMTS["int4" if name == "int4pc" else name]
-    group = 0 if name == "int4pc" else 64
+    fmt, group = _fmt_group(name)
     n, k = nk
     _say(f"gemm {name} n={n} k={k} m={m}")
     p = _quant(fmt, (n, k), (3, fmt, group, n, k), group=group)
@@ -173,8 +178,7 @@ def test_tiled_gemm_repeatable_short_k(wq, name):
     # 32-column blocks here, intermittently).
     import torch
 
-    fmt = FMTS["int4" if name == "int4pc" else name]
-    group = 0 if name == "int4pc" else 64
+    fmt, group = _fmt_group(name)
     for k in (64, 128, 192):
         n, m = 320, 64
         p = _quant(fmt, (n, k), (21, fmt, group, k), group=group)
@@ -198,8 +202,7 @@ def test_gemm_decodes_every_weight_bit_exact(wq, name):
     # must equal the oracle's decoded bits.
     import torch
 
-    fmt = FMTS["int4" if name == "int4pc" else name]
-    group = 0 if name == "int4pc" else 64
+    fmt, group = _fmt_group(name)
     n, k = 48, 320
     p = _quant(fmt, (n, k), (7, fmt, group), group=group)
     ref = oracle.dequantize(p)
@@ -264,6 +267,9 @@ MOE_CASES = [
     ("ccqh", 8, 576, 320, 40, 4),
     ("ccq432", 4, 576, 192, 64, 2),     # 32 rows per expert on average
     ("ccqh", 8, 512, 320, 200, 4),
+    ("int8", 8, 256, 192, 12, 2),
+    ("int8pc", 4, 320, 192, 70, 2),      # tiled
+    ("int8", 4, 256, 128, 96, 2),        # group-64 INT8: decode-streaming kernels at every size
 ]
 
 
@@ -272,8 +278,7 @@ def test_moe_ffn_parity(wq, case):
     import torch
 
     name, E, H, I, T, topk = case
-    fmt = FMTS["int4" if name == "int4pc" else name]
-    group = 0 if name == "int4pc" else 64
+    fmt, group = _fmt_group(name)
     _say(f"moe {case}")
     gate = _quant(fmt, (E, I, H), (9, 1, E, H, I), group=group)
     up = _quant(fmt, (E, I, H), (9, 2, E, H, I), group=group)
@@ -328,8 +333,7 @@ def test_tiled_gemm_decodes_every_weight_bit_exact(wq):
     import torch
 
     for name in ALL:
-        fmt = FMTS["int4" if name == "int4pc" else name]
-        group = 0 if name == "int4pc" else 64
+        fmt, group = _fmt_group(name)
         n, k = 136, 320
         p = _quant(fmt, (n, k), (17, fmt, group), group=group)
         ref = oracle.dequantize(p)
@@ -342,14 +346,13 @@ def test_tiled_gemm_decodes_every_weight_bit_exact(wq):
             assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + w])), f"{name} columns {c0}.."
 
 
-@pytest.mark.parametrize("name", ["ccq", "int4pc", "ccq432", "ccqh"])
+@pytest.mark.parametrize("name", ["ccq", "int4pc", "ccq432", "ccqh", "int8pc"])
 def test_moe_prefill_skewed_routing(wq, name):
     # Zipf-biased routing as in the prefill workload, at reduced sizes: most rows go to the
     # first experts (several 128-row tiles), the tail experts get a few rows or none.
     import torch
 
-    fmt = FMTS["int4" if name == "int4pc" else name]
-    group = 0 if name == "int4pc" else 64
+    fmt, group = _fmt_group(name)
     E, H, I, T, topk = 16, 512, 256, 384, 4
     gate = _quant(fmt, (E, I, H), (18, 1), group=group)
     up = _quant(fmt, (E, I, H), (18, 2), group=group)

@@ -26,7 +26,7 @@ WQ_ERR_RANGE = -4
 WQ_ERR_WORKSPACE = -5
 WQ_ERR_HIP = -6
 
-FMT_INT4, FMT_INT2_AFFINE, FMT_CCQ2, FMT_CCQ432, FMT_CCQ_HYBRID = 1, 2, 3, 4, 5
+FMT_INT4, FMT_INT2_AFFINE, FMT_CCQ2, FMT_CCQ432, FMT_CCQ_HYBRID, FMT_INT8 = 1, 2, 3, 4, 5, 6
 
 # Every symbol include/wq.h declares.
 EXPORTS = ("wq_dequantize", "wq_gemm", "wq_moe_workspace_bytes", "wq_moe_route", "wq_moe_ffn",

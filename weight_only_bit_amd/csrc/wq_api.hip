@@ -33,10 +33,11 @@ wq_status hip_status(hipError_t e, const char* what) {
   return fail(WQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Formats the tiled (many-row) kernels implement (all of them).
-bool has_tiled(int32_t f) {
-  return f == WQ_FMT_INT4 || f == WQ_FMT_INT2_AFFINE || f == WQ_FMT_CCQ2 || f == WQ_FMT_CCQ432 ||
-         f == WQ_FMT_CCQ_HYBRID;
+// Weights the tiled (many-row) kernels implement: every format but group-64 INT8, whose
+// packed data (64 bytes per row per step plus scales) leaves no LDS for a staging ring next to
+// the activation ring; it runs the decode-streaming kernels for every row count.
+bool has_tiled(const wq_weight* w) {
+  return w->format != WQ_FMT_INT8 || w->group == 0;
 }
 
 bool is_ccq(int32_t f) {
@@ -47,6 +48,7 @@ bool is_ccq(int32_t f) {
 int64_t row_code_bytes(const wq_weight* w) {
   switch (w->format) {
     case WQ_FMT_INT4: return w->k / 2;
+    case WQ_FMT_INT8: return w->k;
     case WQ_FMT_CCQ432: return w->k / 64 * 22;
     case WQ_FMT_CCQ_HYBRID: return w->k / 64 * 20;
     default: return w->k / 4;
@@ -79,6 +81,12 @@ wq_status check_weight(const wq_weight* w, const char* what) {
     case WQ_FMT_INT4:
       if (w->group != 64 && w->group != 0)
         return fail(WQ_ERR_UNSUPPORTED, "%s: INT4 group must be 64 or 0 (per channel)", what);
+      if (!w->scales) return fail(WQ_ERR_ARG, "%s: null scales", what);
+      if (!aligned16(w->scales)) return fail(WQ_ERR_ALIGN, "%s: scales not 16-byte aligned", what);
+      break;
+    case WQ_FMT_INT8:
+      if (w->group != 64 && w->group != 0)
+        return fail(WQ_ERR_UNSUPPORTED, "%s: INT8 group must be 64 or 0 (per channel)", what);
       if (!w->scales) return fail(WQ_ERR_ARG, "%s: null scales", what);
       if (!aligned16(w->scales)) return fail(WQ_ERR_ALIGN, "%s: scales not 16-byte aligned", what);
       break;
@@ -229,7 +237,7 @@ wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y,
   if (!aligned16(x) || !aligned16(y)) return fail(WQ_ERR_ALIGN, "wq_gemm: x or y not 16-byte aligned");
   if (m > (1ll << 31)) return fail(WQ_ERR_UNSUPPORTED, "wq_gemm: m must be below 2^31");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (m > kSkinnyMaxRows && has_tiled(w->format)) {
+  if (m > kSkinnyMaxRows && has_tiled(w)) {
     wq::TiledArgs t{};
     t.w0 = dev_weight(w);
     t.w1 = t.w0;
@@ -315,7 +323,7 @@ int moe_row_tiles(int64_t t, int32_t topk, int64_t experts) {
 }
 
 bool moe_tiled(const wq_weight* w, int64_t t, int32_t topk) {
-  return has_tiled(w->format) && (double)t * topk / (double)w->experts >= kMoeTiledRows;
+  return has_tiled(w) && (double)t * topk / (double)w->experts >= kMoeTiledRows;
 }
 
 int64_t moe_tile_bound(int64_t t, int32_t topk, int64_t experts) {

@@ -17,7 +17,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum { FMT_INT4 = 1, FMT_AFFINE2 = 2, FMT_CCQ2 = 3, FMT_CCQ432 = 4, FMT_CCQH = 5 };
+enum { FMT_INT4 = 1, FMT_AFFINE2 = 2, FMT_CCQ2 = 3, FMT_CCQ432 = 4, FMT_CCQH = 5, FMT_INT8 = 6 };
 
 // The CCQ formats without code cluster: the group scale rides in the last code word.
 __host__ __device__ constexpr bool is_alg2(int f) { return f == FMT_CCQ432 || f == FMT_CCQH; }
@@ -175,6 +175,20 @@ __device__ __forceinline__ void int4_decode16(uint32_t w0, uint32_t w1, float s2
     p[4 * h + 1] = cvt_pk_bf16(mix_lo(q2, s24, m8s), mix_lo(q3, s24, m8s));
     p[4 * h + 2] = cvt_pk_bf16(mix_hi(q0, s24, m8s), mix_hi(q1, s24, m8s));
     p[4 * h + 3] = cvt_pk_bf16(mix_hi(q2, s24, m8s), mix_hi(q3, s24, m8s));
+  }
+}
+
+// INT8: 16 signed bytes (k order).  XOR 0x80 biases a byte q to q + 128 in 0..255 (< 1024, so
+// an f16 subnormal), value = fl((q + 128) s - 128 s); s24 = s * 2^24, m128s = -128 s.
+__device__ __forceinline__ void int8_decode16(const u32x4& w, float s24, float m128s,
+                                              uint32_t (&p)[8]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t x = w[d] ^ 0x80808080u;
+    const uint32_t ev = x & 0x00FF00FFu;         // bytes 0, 2
+    const uint32_t od = (x >> 8) & 0x00FF00FFu;  // bytes 1, 3
+    p[2 * d] = cvt_pk_bf16(mix_lo(ev, s24, m128s), mix_lo(od, s24, m128s));
+    p[2 * d + 1] = cvt_pk_bf16(mix_hi(ev, s24, m128s), mix_hi(od, s24, m128s));
   }
 }
 

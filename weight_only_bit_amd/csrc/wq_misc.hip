@@ -11,6 +11,7 @@ namespace {
 // Dequantize: one thread per 16 consecutive weights of a row (one 64-bit or 32-bit code load,
 // two 16-byte stores), bit-exact with the format definitions:
 //   INT4:   bf16(f32(q) * s)                 (lesson E6.4: x_hat = s q, zero point 0)
+//   INT8:   bf16(f32(q) * s)                 (the same formula for a signed byte)
 //   AFFINE: bf16(f32(q - z) * s)             (lesson E6.4: x_hat = s (q - z))
 //   CCQ2:   s = f32(s_q) * super; C = expand(C'); u = (C >> shift) & 0x3F;
 //           bf16(f32(u - zp) * s)           (CCQ, "Dequantization with Code Cluster")
@@ -34,6 +35,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DevWeight w, int64_t
     for (int i = 0; i < 16; ++i) {
       const uint32_t word = i < 8 ? c.x : c.y;
       v[i] = int4_value((word >> (4 * (i & 7))) & 0xFu, s);
+    }
+  } else if constexpr (FMT == FMT_INT8) {
+    const u32x4 c = *reinterpret_cast<const u32x4*>(w.codes + row * w.k + k0);
+    const float s = bf16_bits_to_f32(w.group ? w.scales[row * G + g] : w.scales[row]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t q = (int32_t)(int8_t)(uint8_t)(c[i >> 2] >> (8 * (i & 3)));
+      v[i] = (float)q * s;
     }
   } else if constexpr (FMT == FMT_AFFINE2) {
     const uint32_t c = *reinterpret_cast<const uint32_t*>(w.codes + row * (w.k / 4) + (k0 >> 2));
@@ -234,6 +243,8 @@ hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t
     hipLaunchKernelGGL(dequant_kernel<FMT_INT4>, grid, dim3(256), 0, stream, w, rows, out);
   else if (fmt == FMT_AFFINE2)
     hipLaunchKernelGGL(dequant_kernel<FMT_AFFINE2>, grid, dim3(256), 0, stream, w, rows, out);
+  else if (fmt == FMT_INT8)
+    hipLaunchKernelGGL(dequant_kernel<FMT_INT8>, grid, dim3(256), 0, stream, w, rows, out);
   else if (fmt == FMT_CCQ432)
     hipLaunchKernelGGL(dequant_alg2_kernel<FMT_CCQ432>, grid, dim3(256), 0, stream, w, rows, out);
   else if (fmt == FMT_CCQH)

@@ -32,13 +32,15 @@ namespace {
 
 constexpr int KCT_BASE = 512;  // activation columns per LDS chunk (all K-parts together)
 constexpr int FMT_INT4PC = 8;  // INT4 with one scale per output channel (kernel variant)
+constexpr int FMT_INT8PC = 9;  // INT8 with one scale per output channel (kernel variant)
 
 __host__ __device__ constexpr bool is_int4(int f) { return f == FMT_INT4 || f == FMT_INT4PC; }
+__host__ __device__ constexpr bool is_int8(int f) { return f == FMT_INT8 || f == FMT_INT8PC; }
 
 // Weights one lane decodes per step: 16 bytes of codes, or one group of the CCQ formats
 // without code cluster (22 or 20 bytes).
 template <int FMT>
-__host__ __device__ constexpr int lane_weights() { return is_int4(FMT) ? 32 : 64; }
+__host__ __device__ constexpr int lane_weights() { return is_int8(FMT) ? 16 : is_int4(FMT) ? 32 : 64; }
 
 // Columns per wave per LDS chunk: at least one step (4 lanes x lane_weights).
 template <int FMT, int KSPLIT>
@@ -94,6 +96,16 @@ __device__ __forceinline__ WaveW<FMT> wave_weight(const DevWeight& w, int64_t e,
     } else {
       v.fin = bf16_bits_to_f32(w.scales[e * n + row]);
     }
+  } else if constexpr (is_int8(FMT)) {
+    // a step is one group: lane kb holds weights 16 kb .. 16 kb + 15 of group gb + j
+    v.codes = make_rsrc(w.codes + e * n * k, n * k);
+    v.row_codes = (int32_t)(row * k + gb * 64 + kb * 16);
+    if constexpr (FMT == FMT_INT8) {
+      v.scales = make_rsrc(w.scales + e * n * G, n * G * 2);
+      v.row_scales = (int32_t)(row * G * 2 + gb * 2);
+    } else {
+      v.fin = bf16_bits_to_f32(w.scales[e * n + row]);
+    }
   } else if constexpr (FMT == FMT_AFFINE2) {
     v.codes = make_rsrc(w.codes + e * n * (k / 4), n * (k / 4));
     v.row_codes = (int32_t)(row * (k / 4) + gb * 16 + kb * 16);  // group gb + 4 j + kb
@@ -143,7 +155,9 @@ __device__ __forceinline__ void load_raw(Raw<FMT>& r, const WaveW<FMT>& v, int32
     return;
   }
   r.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v.codes, v.row_codes, st * 64, 0));
-  if constexpr (FMT == FMT_INT4) {
+  if constexpr (FMT == FMT_INT8) {
+    r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 2, 0);
+  } else if constexpr (FMT == FMT_INT4) {
     r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 4, 0);
   } else if constexpr (FMT == FMT_AFFINE2) {
     r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 8, 0);
@@ -327,6 +341,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
         } else if constexpr (FMT == FMT_INT4PC) {
           s24 = fin24;
           mzs = fin24 * (-8.0f / kTwo24);
+        } else if constexpr (FMT == FMT_INT8) {
+          s24 = bf16_bits_to_f32(rw.scale & 0xFFFFu) * kTwo24;
+          mzs = s24 * (-128.0f / kTwo24);
+        } else if constexpr (FMT == FMT_INT8PC) {
+          s24 = fin24;
+          mzs = fin24 * (-128.0f / kTwo24);
         } else {
           const float s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
           s24 = s * kTwo24;
@@ -340,6 +360,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
             ccq_decode16<CLAMP>(rw.codes[q], cs24, W.cz, s24, mzs, p);
           } else if constexpr (is_int4(FMT)) {
             int4_decode16(rw.codes[2 * q], rw.codes[2 * q + 1], s24, mzs, p);
+          } else if constexpr (is_int8(FMT)) {
+            int8_decode16(rw.codes, s24, mzs, p);
           } else {
             affine2_decode16(rw.codes[q], s24, mzs, p);
           }
@@ -489,6 +511,10 @@ hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const Skinn
       return launch_fmt<FMT_INT4>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
     case FMT_AFFINE2:
       return launch_fmt<FMT_AFFINE2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_INT8:
+      if (args.w0.group == 0)
+        return launch_fmt<FMT_INT8PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+      return launch_fmt<FMT_INT8>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
     case FMT_CCQ432:
       return launch_fmt<FMT_CCQ432>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
     case FMT_CCQH:

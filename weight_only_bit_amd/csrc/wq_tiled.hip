@@ -74,6 +74,7 @@ struct Codes {
   uint32_t scale;  // CCQ: scale byte; INT4 / affine: bf16 bits
   uint32_t zero;   // affine zero point
   u32x2 t;         // (4,3,2): bytes 16..23 of the aligned window; hybrid: bytes 16..19
+  u32x4 c2;        // INT8: the second 16 bytes of the lane's 32 weights
 };
 
 // Where one weight row's packed data lives; the row is copied to LDS by one lane of its wave.
@@ -89,7 +90,9 @@ template <int FMT>
 __device__ __forceinline__ RowSrc row_src(const DevWeight& w, int64_t e, int64_t row) {
   RowSrc r{};
   const int64_t n = w.n, k = w.k, G = k / 64, grow = e * n + row;
-  if (FMT == FMT_INT4) {
+  if (FMT == FMT_INT8) {  // per output channel (group-64 INT8 runs the decode-streaming kernels)
+    r.codes = w.codes + grow * k;
+  } else if (FMT == FMT_INT4) {
     r.codes = w.codes + grow * (k / 2);
     if (w.group) {
       r.scale = reinterpret_cast<const uint8_t*>(w.scales + grow * G);
@@ -122,7 +125,11 @@ template <int FMT>
 __device__ __forceinline__ void cdecode(const Codes<FMT>& p, const RowConst& r, int64_t g,
                                         float mzp24, uint32_t (&o)[16]) {
   uint32_t a[8], b[8];
-  if (FMT == FMT_INT4) {
+  if (FMT == FMT_INT8) {
+    const float m128s = r.fin24 * (-128.0f / kTwo24);
+    int8_decode16(p.c, r.fin24, m128s, a);
+    int8_decode16(p.c2, r.fin24, m128s, b);
+  } else if (FMT == FMT_INT4) {
     const float s24 = bf16_bits_to_f32(p.scale & 0xFFFFu) * kTwo24;
     const float m8s = s24 * (-8.0f / kTwo24);
     int4_decode16(p.c.x, p.c.y, s24, m8s, a);
@@ -148,17 +155,20 @@ __device__ __forceinline__ void cdecode(const Codes<FMT>& p, const RowConst& r, 
 // then one dword per row for the scale, then (affine) one for the zero point.  (4,3,2) and
 // hybrid: the first 16 bytes of each row's group window, then one (hybrid) or two ((4,3,2))
 // dwords per row for the rest.
+// INT8 (per channel): each row's 64 bytes as four 16-byte pieces (piece i at 1024 i), no scale
+// (the row's scale is read once); two stages fill the 160 KB with the activation ring exactly.
 template <int FMT>
 struct CodeRing {
-  static constexpr int CODE_BYTES = (FMT == FMT_INT4 ? 2 : 1) * 64 * 16;
+  static constexpr int CODE_BYTES = (FMT == FMT_INT8 ? 4 : FMT == FMT_INT4 ? 2 : 1) * 64 * 16;
   static constexpr int WAVE_BYTES =
-      CODE_BYTES + 256 * ((FMT == FMT_AFFINE2 || FMT == FMT_CCQ432) ? 2 : 1);
+      CODE_BYTES + (FMT == FMT_INT8 ? 0 : 256 * ((FMT == FMT_AFFINE2 || FMT == FMT_CCQ432) ? 2 : 1));
   static constexpr int STAGE_BYTES = 4 * WAVE_BYTES;
-  static constexpr int DEPTH = (FMT == FMT_INT4) ? 2 : 4;  // stages (fits 160 KB with A)
+  static constexpr int DEPTH = (FMT == FMT_INT4 || FMT == FMT_INT8) ? 2 : 4;  // fits 160 KB with A
   static constexpr int AHEAD = DEPTH - 1 > 2 ? DEPTH - 1 : 2;  // steps between copy and decode
   // memory instructions per step per lane: codes, scale, zero / window pieces
-  static constexpr int VMEM = is_alg2(FMT) ? (FMT == FMT_CCQ432 ? 3 : 2)
-                                           : (FMT == FMT_INT4 ? 2 : 1) + 1 + (FMT == FMT_AFFINE2 ? 1 : 0);
+  static constexpr int VMEM = FMT == FMT_INT8 ? 4
+                             : is_alg2(FMT) ? (FMT == FMT_CCQ432 ? 3 : 2)
+                                            : (FMT == FMT_INT4 ? 2 : 1) + 1 + (FMT == FMT_AFFINE2 ? 1 : 0);
 };
 
 // Row tiles.  An expert's (or the dense matrix's) rows are covered by full 256-row tiles; the
@@ -214,6 +224,10 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
       const DevWeight& w = (MODE == MODE_GATEUP && j == 1) ? args.w1 : args.w0;
       const int64_t grow = e * w.n + (wrow[j] < N ? wrow[j] : N - 1);
       rc[j] = RowConst{w.code_scale[grow] * kTwo24, w.code_zero[grow], w.super_scale[grow] * kTwo24};
+    } else if constexpr (FMT == FMT_INT8) {  // the row's one scale
+      const DevWeight& w = (MODE == MODE_GATEUP && j == 1) ? args.w1 : args.w0;
+      const int64_t grow = e * w.n + (wrow[j] < N ? wrow[j] : N - 1);
+      rc[j] = RowConst{0.f, 0.f, bf16_bits_to_f32(w.scales[grow]) * kTwo24};
     }
   }
   const float mzp24 = -(float)args.w0.zp / kTwo24;
@@ -307,6 +321,14 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
                                          (__attribute__((address_space(3))) void*)(base + 1280), 4, 0, 0);
       return;
     }
+    if constexpr (FMT == FMT_INT8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(rs.codes + g * 64 + 16 * i),
+            (__attribute__((address_space(3))) void*)(base + 1024 * i), 16, 0, 0);
+      return;
+    }
     if constexpr (FMT == FMT_INT4) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rs.codes + g * 32),
                                        (__attribute__((address_space(3))) void*)(base), 16, 0, 0);
@@ -365,6 +387,25 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
       }
       cc[0].c = c0;
       cc[0].t = (u32x2){t0, t1};
+      return;
+    }
+    if constexpr (FMT == FMT_INT8) {  // rows j = 0, 1: pieces 2 kh and 2 kh + 1
+      const uint32_t ia = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
+          base + kh * 2048 + l32 * 16);
+      u32x4 a0, a1, b0, b1;
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %4 offset:1024\n\t"
+          "ds_read_b128 %2, %4 offset:512\n\t"
+          "ds_read_b128 %3, %4 offset:1536\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+          : "v"(ia)
+          : "memory");
+      cc[0].c = a0;
+      cc[0].c2 = a1;
+      cc[1].c = b0;
+      cc[1].c2 = b1;
       return;
     }
     const uint32_t ca = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(
@@ -582,9 +623,17 @@ void tiled_kernel(const TiledArgs args) {
   using Ring = CodeRing<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t sC0[Ring::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t sC1[Ring::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sC2[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sC3[Ring::DEPTH > 2 ? Ring::STAGE_BYTES : 16];
-  __shared__ int32_t s_tile[3];
+  uint8_t* sC2 = sC0;  // stages 2 and 3 exist only for four-stage rings
+  uint8_t* sC3 = sC1;
+  if constexpr (Ring::DEPTH > 2) {
+    __shared__ __attribute__((aligned(16))) uint8_t sC2_[Ring::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t sC3_[Ring::STAGE_BYTES];
+    sC2 = sC2_;
+    sC3 = sC3_;
+  }
+  // The MoE tile lookup result lives in the first bytes of packed-data stage 1 (INT8's rings
+  // fill the LDS exactly); every thread has read it before any copy writes that stage.
+  int32_t* s_tile = reinterpret_cast<int32_t*>(sC1);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
 
@@ -655,6 +704,7 @@ void tiled_kernel(const TiledArgs args) {
     const int64_t cnt = args.offsets[e + 1] - base;
     row0 = base + class_row0(mt, cnt, s_tile[2]);
     rows = base + cnt - row0 < BM ? base + cnt - row0 : BM;
+    __syncthreads();  // s_tile read by every thread before stage 1 is overwritten
   }
   const CodeStages cs{{sC0, sC1, sC2, sC3}};
   switch (mt) {
@@ -686,6 +736,9 @@ hipError_t launch_mode(int fmt, const TiledArgs& a, int64_t row_tiles, hipStream
     case FMT_INT4: return launch_t<FMT_INT4, MODE>(a, row_tiles, s);
     case FMT_AFFINE2: return launch_t<FMT_AFFINE2, MODE>(a, row_tiles, s);
     case FMT_CCQ2: return launch_t<FMT_CCQ2, MODE>(a, row_tiles, s);
+    case FMT_INT8:
+      if (a.w0.group != 0) return hipErrorInvalidValue;  // per channel only
+      return launch_t<FMT_INT8, MODE>(a, row_tiles, s);
     case FMT_CCQ432: return launch_t<FMT_CCQ432, MODE>(a, row_tiles, s);
     case FMT_CCQH: return launch_t<FMT_CCQH, MODE>(a, row_tiles, s);
     default: return hipErrorInvalidValue;
