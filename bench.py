@@ -364,7 +364,8 @@ def moe_prefill(args):
 
 
 def dense_decode(args):
-    """One 4096 x 4096 linear at 1, 8 and 32 rows, CCQ and 2-bit affine; each call reads one of
+    """One 4096 x 4096 linear at 1, 8 and 32 rows, CCQ, 2-bit affine and WINT8 (per channel, the
+    deployment's dense layers); each call reads one of
     enough distinct weight copies (>= 1 GiB in total) that the 256 MB last-level cache holds no
     weights between calls."""
     import numpy as np
@@ -377,12 +378,13 @@ def dense_decode(args):
     dev = torch.device("cuda:0")
     N = Kd = 4096
     res = {}
-    for fmt, name in ((wq.FMT_CCQ2, "ccq"), (wq.FMT_INT2_AFFINE, "affine2")):
+    for fmt, name, group in ((wq.FMT_CCQ2, "ccq", 64), (wq.FMT_INT2_AFFINE, "affine2", 64),
+                             (wq.FMT_INT8, "int8pc", 0)):
         one = None
         copies = []
         for c in range(256):
-            arr = synth.random_packed_device(fmt, 1, N, Kd, 3000 + c)
-            w = wq.PackedWeight(fmt, N, Kd, 1, 64, *(arr.get(f) for f in (
+            arr = synth.random_packed_device(fmt, 1, N, Kd, 3000 + c, group=group)
+            w = wq.PackedWeight(fmt, N, Kd, 1, group, *(arr.get(f) for f in (
                 "codes", "scales", "zeros", "qscale", "super_scale", "code_scale", "code_zero")), 32)
             copies.append(w)
             one = w.nbytes()
@@ -413,15 +415,15 @@ def dense_decode(args):
 # The operator tables of the CCQ paper's inference-performance section (execution time in ms on
 # one NVIDIA H20; quoted as context only, another machine's numbers): GEMV input x output at
 # M = 1 and 4 (columns WINT2-standard, CCQ) and grouped GEMM groups x output x input at M = 1,
-# 4, 16, 64 (columns W4A16, W2A16-CCQ).
+# 4, 16, 64 (columns W8A16, W4A16, W2A16-CCQ).
 PAGES_GEMV_MS = {(4096, 4096, 1): (0.027, 0.034), (4096, 1024, 1): (0.015, 0.017),
                  (8192, 8192, 1): (0.073, 0.090), (8192, 1024, 1): (0.019, 0.022),
                  (4096, 4096, 4): (0.028, 0.035), (4096, 1024, 4): (0.015, 0.017),
                  (8192, 8192, 4): (0.076, 0.104), (8192, 1024, 4): (0.019, 0.024)}
-PAGES_GROUPED_MS = {(7168, 512, 1): (0.030, 0.021), (1024, 7168, 1): (0.068, 0.058),
-                    (7168, 512, 4): (0.035, 0.027), (1024, 7168, 4): (0.199, 0.166),
-                    (7168, 512, 16): (0.071, 0.059), (1024, 7168, 16): (0.624, 0.527),
-                    (7168, 512, 64): (0.193, 0.161), (1024, 7168, 64): (1.628, 1.386)}
+PAGES_GROUPED_MS = {(7168, 512, 1): (0.044, 0.030, 0.021), (1024, 7168, 1): (0.100, 0.068, 0.058),
+                    (7168, 512, 4): (0.053, 0.035, 0.027), (1024, 7168, 4): (0.315, 0.199, 0.166),
+                    (7168, 512, 16): (0.104, 0.071, 0.059), (1024, 7168, 16): (1.052, 0.624, 0.527),
+                    (7168, 512, 64): (0.297, 0.193, 0.161), (1024, 7168, 64): (2.655, 1.628, 1.386)}
 
 
 def pages_shapes(args):
@@ -429,7 +431,7 @@ def pages_shapes(args):
     2-bit affine (the WINT2-standard column) and CCQ.  Grouped GEMM: 256 experts, M tokens each
     routed to 8 distinct experts uniformly; output x input 1024 x 7168 is the fused gate+up
     product (2 x 512 outputs per pair, wq_moe_gate_up) and 7168 x 512 the down product
-    (wq_moe_down), INT4 g64 (W4A16) and CCQ (W2A16).  Every call reads weights that are not in
+    (wq_moe_down), INT8 per channel (W8A16), INT4 g64 (W4A16) and CCQ (W2A16).  Every call reads weights that are not in
     the 256 MB last-level cache: GEMVs rotate over >= 1 GiB of weight copies, grouped products
     over 64 routing tables (each touches 8 M of the 256 experts)."""
     import numpy as np
@@ -473,7 +475,8 @@ def pages_shapes(args):
 
     grouped = {}
     E, topk = 256, 8
-    for fmt, name, group in ((wq.FMT_INT4, "w4a16", 64), (wq.FMT_CCQ2, "w2a16_ccq", 64)):
+    for fmt, name, group in ((wq.FMT_INT8, "w8a16", 0), (wq.FMT_INT4, "w4a16", 64),
+                             (wq.FMT_CCQ2, "w2a16_ccq", 64)):
         g = synth.random_packed_device(fmt, E, 512, 7168, 7101, group=group)
         u = synth.random_packed_device(fmt, E, 512, 7168, 7102, group=group)
         dn = synth.random_packed_device(fmt, E, 7168, 512, 7103, group=group)
@@ -499,7 +502,8 @@ def pages_shapes(args):
                 key = f"256x{o}x{i_}_m{m}"
                 grouped.setdefault(key, {})[name] = {"us": round(us, 2),
                                                      "GB/s": round(touched * per / (us * 1e-6) / 1e9, 1)}
-                grouped[key]["pages_h20_ms"] = dict(zip(("w4a16", "w2a16_ccq"), PAGES_GROUPED_MS[(o, i_, m)]))
+                grouped[key]["pages_h20_ms"] = dict(zip(("w8a16", "w4a16", "w2a16_ccq"),
+                                                        PAGES_GROUPED_MS[(o, i_, m)]))
                 grouped[key]["experts_touched"] = round(touched, 1)
         del gw, uw, dw
         torch.cuda.empty_cache()
