@@ -75,11 +75,12 @@ def parse():
                          "2.75 bpw; ccqh = hybrid (3,3,2)+(3,4,2), 2.5 bpw")
     ap.add_argument("--workload", default="moe_stack_decode",
                     choices=["moe_stack_decode", "moe_prefill", "dense_decode", "copy_calibration",
-                             "pages_shapes"],
+                             "pages_shapes", "ccq_encode"],
                     help="moe_stack_decode (default): the 54-layer stack step; moe_prefill: one "
                          "CCQ MoE layer at 4096 tokens with Zipf-skewed routing; dense_decode: "
                          "one 4096x4096 CCQ / 2-bit affine linear at 1, 8, 32 rows; pages_shapes: "
-                         "the GEMV and grouped-GEMM shapes of the CCQ paper's operator tables")
+                         "the GEMV and grouped-GEMM shapes of the CCQ paper's operator tables; "
+                         "ccq_encode: the GPU CCQ encoder on one expert gate tensor")
     return ap.parse_args()
 
 
@@ -125,6 +126,8 @@ def main():
         return copy_calibration(args)
     if args.workload == "pages_shapes":
         return pages_shapes(args)
+    if args.workload == "ccq_encode":
+        return ccq_encode(args)
 
     import numpy as np
     import torch
@@ -513,6 +516,63 @@ def pages_shapes(args):
            "unit": "us", "n_gpus": 1, "steps": args.steps, "higher_is_better": False, "dtype": "bf16",
            "data": "synthetic", "config": {"workload": "pages_shapes"}, "gemv": gemv, "grouped_gemm": grouped,
            "note": "pages_h20_ms are the pages' own H20 timings, context only"}
+    print(json.dumps(out), flush=True)
+
+
+FP64_PEAK_TFLOPS = 78.6  # MI355X vector fp64
+
+
+def ccq_encode(args):
+    """The CCQ (6,4,3) code-cluster encoder (wq_quantize_ccq, refine on) on the gate tensor of
+    one MoE layer: 64 experts x 3584 x 8192 fp32 weights ~ N(0, 0.02) drawn on the GPU.  Rate in
+    weights/s; roofline against the fp64 vector peak with about 5,050 fp64 operations per
+    4-weight vector (the 960 of the trellis search and 4,096 of the 256-candidate re-pick)."""
+    import numpy as np
+    import torch
+
+    import weight_only_bit_amd as wq
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    E, n, k = 64, 3584, 8192
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    w = torch.randn((E, n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02
+    for _ in range(max(args.warmup, 1)):
+        wq.wq_quantize_ccq(w)
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(args.steps):
+        wq.wq_quantize_ccq(w)
+    en.record()
+    torch.cuda.synchronize()
+    ms = st.elapsed_time(en) / args.steps
+    weights = E * n * k
+    flops = weights / 4 * (960 + 4096)
+    tf = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        rows = 256
+        sample = w[0, :rows].cpu().numpy()
+        t1 = time.perf_counter()
+        oracle.quantize(sample, oracle.CCQ, refine=True)
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(rows * k / dt / 1e6, 3), "unit": "M weights/s",
+               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+               "sample": f"{rows} rows x {k} of expert 0, refine on, {dt:.1f} s"}
+    log(f"encode {ms:.1f} ms for {weights / 1e9:.2f} G weights ({weights / (ms * 1e-3) / 1e9:.1f} G weights/s), "
+        f"{tf:.1f} fp64 TFLOP/s")
+    out = {"metric": "CCQ encode rate (weights/s)", "value": round(weights / (ms * 1e-3), 1),
+           "unit": "weights/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 3), "higher_is_better": True, "dtype": "f64", "data": "synthetic",
+           "config": {"workload": "ccq_encode", "experts": E, "rows": n, "k": k, "refine": True},
+           "roofline": {"kernel": "ccq_encode_kernel<true>", "bound": "alu", "achieved": round(tf, 2),
+                        "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / FP64_PEAK_TFLOPS, 4),
+                        "traffic": None, "algorithmic_flops_per_launch": flops},
+           "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
 

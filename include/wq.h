@@ -170,6 +170,27 @@ wq_status wq_moe_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t*
 wq_status wq_moe_combine(const float* d, const float* topk_weights, int64_t t, int32_t topk,
                          int64_t hidden, uint16_t* y, void* stream);
 
+/* CCQ (6,4,3) code-cluster encoder (CCQ paper, algorithm "Convolutional Code Quantization" of
+ * section 3.1, section 3.3 Eq. 1, section 3.4 scale compression): fp32 weights w[n][k] (device,
+ * row-major; an MoE tensor is n = experts x rows) -> the WQ_FMT_CCQ2 arrays of the layout above
+ * (codes u8[n][k/4], qscale u8[n][(k/64+1)/2], super_scale, code_scale, code_zero f32[n], all
+ * device memory owned by the caller).  Per row, groups of 64:
+ *   s_g = absmax_g / 31; super = f32(max_g s_g / 15) (1 for a zero row);
+ *   s_q = clip(round(s_g / super), 1, 15); s = f32(s_q) * super;
+ *   C = the 15-bit code minimizing sum_j (v_j - (u_j - zp) s)^2 over the vector's 4 weights
+ *       (u_j: states at shifts 9, 6, 3, 0; ties to the smallest code);
+ *   beta = min C, alpha = f32((max C - min C) / 255) (1 if all codes are equal);
+ *   C' = clip(round((C - beta) / alpha), 0, 255), or, when refine != 0, the C' in 0..255 whose
+ *       decoded code (round(fmaf(C', alpha, beta)) clamped to [0, 2^15 - 1]) costs least
+ *       (ties to the smallest C').
+ * Costs, ratios and roundings to integers are taken in fp64 (round half to even), so the
+ * outputs are a function of w alone.  Requires k % 64 == 0, k <= 131072 (one workgroup keeps
+ * a row's codes in LDS), zp in 0..127, w 16-byte aligned.  Asynchronous on `stream`, no
+ * allocation. */
+wq_status wq_quantize_ccq(const float* w, int64_t n, int64_t k, int32_t zp, int32_t refine,
+                          uint8_t* codes, uint8_t* qscale, float* super_scale, float* code_scale,
+                          float* code_zero, void* stream);
+
 /* Host helpers for the INT4 storage format (lesson E6.4, "Do it in code"); host memory.
  * wq_pack_int4: two codes per byte, the first in the low nibble, an odd count padded with 0;
  *   out must hold (n+1)/2 bytes; WQ_ERR_RANGE (nothing written) for a code outside -8..7.

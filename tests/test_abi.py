@@ -139,3 +139,15 @@ def test_moe_argument_checks(wq):
     big = _weight(wq, experts=1000, n=I, k=H)
     assert call(big, big, _weight(wq, experts=1000, n=H, k=I), need) == -2
     assert L.wq_moe_route(ids, T, K, 0, ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000), None, 0, None) == -1
+
+
+def test_quantize_ccq_argument_checks(wq):
+    L = wq.lib()
+    p = [ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000)]
+    call = lambda n, k, zp, w=p[0]: L.wq_quantize_ccq(w, n, k, zp, 1, *p[1:], None)
+    assert call(4, 100, 32) == -2                  # k not a multiple of 64
+    assert call(4, 131072 + 64, 32) == -2          # a row's codes must fit the LDS
+    assert call(0, 256, 32) == -1
+    assert call(4, 256, 200) == -2
+    assert call(4, 256, 32, w=None) == -1
+    assert call(4, 256, 32, w=ctypes.c_void_p(0x10008)) == -3

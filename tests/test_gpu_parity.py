@@ -394,3 +394,29 @@ def test_gemm_ccq_clamped_rows_bit_exact(wq):
             x[np.arange(w), c0 + np.arange(w)] = 0x3F80
             y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
             assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + w])), (m, c0)
+
+
+# ---------------------------------------------------------------------------------------------
+# CCQ encoder on the GPU: bit-identical to the oracle's quantizer
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,zp,refine", [((1, 40, 320), 32, True), ((1, 40, 320), 32, False),
+                                             ((2, 24, 1024), 32, True), ((1, 6, 8192), 32, True),
+                                             ((1, 16, 448), 0, True), ((1, 16, 448), 16, False)])
+def test_quantize_ccq_matches_oracle(wq, shape, zp, refine):
+    import torch
+
+    E, n, k = shape
+    _say(f"ccq encode {shape} zp={zp} refine={refine}")
+    w = synth.weights_f32(shape, 33, E, n, k)
+    w[0, 0] = 0.0                                  # a zero row: super scale 1
+    w[0, 1] = 0.01                                 # a constant row: one code, code scale 1
+    w[0, 2, 5] = 0.9                               # an outlier
+    ref = oracle.quantize(w, oracle.CCQ, refine=refine, zp=zp)
+    got = wq.wq_quantize_ccq(torch.from_numpy(w).cuda(), zp=zp, refine=refine)
+    for name in ("codes", "qscale", "super_scale", "code_scale", "code_zero"):
+        g = getattr(got, name).cpu().numpy()
+        r = getattr(ref, name).reshape(g.shape)
+        assert g.dtype.itemsize == r.dtype.itemsize, name
+        assert np.array_equal(g.view(np.uint8), r.view(np.uint8)), \
+            f"{name}: {(g.view(np.uint8) != r.view(np.uint8)).sum()} bytes differ"

@@ -31,7 +31,7 @@ FMT_INT4, FMT_INT2_AFFINE, FMT_CCQ2, FMT_CCQ432, FMT_CCQ_HYBRID, FMT_INT8 = 1, 2
 # Every symbol include/wq.h declares.
 EXPORTS = ("wq_dequantize", "wq_gemm", "wq_moe_workspace_bytes", "wq_moe_route", "wq_moe_ffn",
            "wq_moe_gate_up", "wq_moe_down", "wq_moe_combine", "wq_pack_int4", "wq_unpack_int4",
-           "wq_packed_size", "wq_status_string", "wq_last_error")
+           "wq_packed_size", "wq_status_string", "wq_last_error", "wq_quantize_ccq")
 
 
 class WqError(RuntimeError):
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "wq_moe_gate_up": (i32, [vp, i64, vp, vp, i32, W, W, vp, vp]),
             "wq_moe_down": (i32, [vp, i64, i32, vp, vp, W, vp, vp]),
             "wq_moe_combine": (i32, [vp, vp, i64, i32, i64, vp, vp]),
+            "wq_quantize_ccq": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]),
             "wq_pack_int4": (i32, [vp, i64, vp]),
             "wq_unpack_int4": (i32, [vp, i64, vp]),
             "wq_packed_size": (i64, [i64, i32]),
@@ -260,6 +261,27 @@ def wq_moe_combine(d, topk_weights, y=None):
     _check(lib().wq_moe_combine(_ptr(d), _ptr(topk_weights), t, topk, hidden, _ptr(y), _stream()),
            "wq_moe_combine")
     return y
+
+
+def wq_quantize_ccq(w, zp: int = 32, refine: bool = True) -> PackedWeight:
+    """CCQ (6,4,3) code-cluster encoding of fp32 weights [n, k] or [E, n, k] on the GPU."""
+    import torch
+
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+    E, n, k = w.shape
+    w = w.contiguous().float()
+    dev = w.device
+    rows = E * n
+    G = k // 64
+    codes = torch.empty((E, n, k // 4), dtype=torch.uint8, device=dev)
+    qscale = torch.empty((E, n, (G + 1) // 2), dtype=torch.uint8, device=dev)
+    sup = torch.empty((E, n), dtype=torch.float32, device=dev)
+    cs = torch.empty((E, n), dtype=torch.float32, device=dev)
+    cz = torch.empty((E, n), dtype=torch.float32, device=dev)
+    _check(lib().wq_quantize_ccq(_ptr(w), rows, k, zp, int(bool(refine)), _ptr(codes), _ptr(qscale),
+                                 _ptr(sup), _ptr(cs), _ptr(cz), _stream()), "wq_quantize_ccq")
+    return PackedWeight(FMT_CCQ2, n, k, E, 64, codes, None, None, qscale, sup, cs, cz, zp)
 
 
 # ---------------------------------------------------------------------------------------------

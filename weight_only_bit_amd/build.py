@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libwq.so")
-SOURCES = ["wq_api.hip", "wq_misc.hip", "wq_skinny.hip", "wq_tiled.hip"]
+SOURCES = ["wq_api.hip", "wq_misc.hip", "wq_skinny.hip", "wq_tiled.hip", "wq_encode.hip"]
 ARCH = os.environ.get("WQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

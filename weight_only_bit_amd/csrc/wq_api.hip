@@ -226,6 +226,22 @@ wq_status wq_dequantize(const wq_weight* w, uint16_t* out, void* stream) {
                     "wq_dequantize launch");
 }
 
+wq_status wq_quantize_ccq(const float* w, int64_t n, int64_t k, int32_t zp, int32_t refine,
+                          uint8_t* codes, uint8_t* qscale, float* super_scale, float* code_scale,
+                          float* code_zero, void* stream) {
+  if (n <= 0 || k <= 0) return fail(WQ_ERR_ARG, "wq_quantize_ccq: n and k must be positive");
+  if (k % 64 != 0) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_ccq: k = %lld is not a multiple of 64", (long long)k);
+  if (k > 131072) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_ccq: k = %lld above 131072", (long long)k);
+  if (n > 0x7FFFFFFFll) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_ccq: n must be below 2^31");
+  if (zp < 0 || zp > 127) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_ccq: zero point must lie in 0..127");
+  if (!w || !codes || !qscale || !super_scale || !code_scale || !code_zero)
+    return fail(WQ_ERR_ARG, "wq_quantize_ccq: null pointer");
+  if (!aligned16(w)) return fail(WQ_ERR_ALIGN, "wq_quantize_ccq: w not 16-byte aligned");
+  return hip_status(wq::launch_ccq_encode(w, n, k, zp, refine != 0, codes, qscale, super_scale,
+                                          code_scale, code_zero, static_cast<hipStream_t>(stream)),
+                    "wq_quantize_ccq launch");
+}
+
 wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y, void* stream) {
   wq_status st = check_weight(w, "wq_gemm");
   if (st != WQ_OK) return st;

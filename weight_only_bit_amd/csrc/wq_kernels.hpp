@@ -54,6 +54,12 @@ struct TiledArgs {
   int32_t experts;
 };
 
+// CCQ (6,4,3) code-cluster encoder: one workgroup per row of w [n][k] (fp32).
+size_t ccq_encode_lds_bytes(int64_t k);
+hipError_t launch_ccq_encode(const float* w, int64_t n, int64_t k, int32_t zp, bool refine,
+                             uint8_t* codes, uint8_t* qscale, float* super_scale,
+                             float* code_scale, float* code_zero, hipStream_t stream);
+
 // Rows of one tile of the tiled kernel.
 int tiled_rows();
 
