@@ -523,19 +523,30 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   read_a(X, 0, std::integral_constant<int, 0>{});
 
   // ---- main loop: iteration g multiplies step g (LDS stage g % 4, B parity g % 2) ----
-  //   before the barrier: slices 0..2 (slice 0 was read last iteration), the next slices'
-  //   reads, and the decode of step g + 1; wait for step g + 1's copy, barrier;
-  //   after it: packed data of step g + AHEAD and activations of step g + 3, read slice 0 of
-  //   step g + 1, slice 3 of step g.
+  //   wait for step g + 1's copies; issue the packed data of step g + AHEAD; then slices 0..2
+  //   (slice 0 was read last iteration), the next slices' reads, the decode of step g + 1 and
+  //   the activation copies of step g + 3 (one after each of the first MFMAs); barrier; read
+  //   slice 0 of step g + 1 under slice 3 of step g.
+  // The activation copies go to the stage of step g - 1, whose last reads every wave made, and
+  // saw return, before the previous iteration's barrier, and the packed data to this wave's own stage of
+  // step g + AHEAD - CD, read at the start of an earlier iteration: neither needs this
+  // iteration's barrier, so both are issued before it, in the shadow of the MFMAs.
   auto iter = [&](int64_t g, auto stc) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
     constexpr int PB = ST & 1;
     // This wave's copies of step g + 1 have landed once at most the previous iteration's
     // memory instructions are outstanding -- or, when the packed data runs only two steps
-    // ahead, its activation copies (issued after its packed data).
+    // ahead, its activation copies (issued after its packed data: the sched_barrier below
+    // keeps that order).
     WQ_WAIT_VMCNT(Ring::AHEAD >= 3 ? VMEM_PER_ITER : MT);
+    // slice 0's fragments (read under the previous iteration's last MFMAs) are complete; saying
+    // so here spares the first MFMA a wait that would also cover the reads issued below
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
     Codes<FMT> cc[2];
     read_codes(cc, std::integral_constant<int, (ST + 1) % CD>{});
+    copy_codes(clamp_step(g + Ring::AHEAD), std::integral_constant<int, (ST + Ring::AHEAD) % CD>{});
+    __builtin_amdgcn_sched_barrier(0);
+    copy_a(clamp_step(g + 3), std::integral_constant<int, (ST + 3) & 3>{});
     read_a(Y, 1, stc);
     mma(X, Bw[PB], 0);
     read_a(X, 2, stc);
@@ -543,10 +554,19 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
     read_a(Y, 3, stc);
     decode_rows(cc, clamp_step(g + 1), Bw[PB ^ 1]);
     mma(X, Bw[PB], 2);
-    // 0x100 LDS read, 0x8 MFMA, 0x2 VALU
+    // 0x100 LDS read, 0x8 MFMA, 0x2 VALU, 0x20 VMEM read (the activation copies).  The copies
+    // go under the first MFMAs of slice 0, before slice 1's fragment reads: the compiler counts
+    // them among the LDS events, and no copy between a read and the wait for it keeps every
+    // wait of the step down to the reads issued after the one it needs.
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
+    }
     __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * MT; ++i) {
+    for (int i = 0; i < MT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
     }
@@ -562,13 +582,13 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
     }
+    // every LDS read of this wave has returned before it arrives: a stage read before this
+    // barrier may be overwritten by any wave's copies in the next iteration
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    copy_codes(clamp_step(g + Ring::AHEAD), std::integral_constant<int, (ST + Ring::AHEAD) % CD>{});
-    copy_a(clamp_step(g + 3), std::integral_constant<int, (ST + 3) & 3>{});
     read_a(X, 0, std::integral_constant<int, (ST + 1) & 3>{});
     mma(Y, Bw[PB], 3);
-    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM reads
     __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * MT, 0);
     __builtin_amdgcn_sched_barrier(0);
