@@ -130,8 +130,8 @@ __device__ __forceinline__ float mix_hi(uint32_t x, float a, float b) {
 template <bool CLAMP = true>
 __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, float s24,
                                              float mzs, uint32_t (&p)[8]) {
-  const uint32_t ev = w & 0x00FF00FFu;         // bytes 0, 2
-  const uint32_t od = (w >> 8) & 0x00FF00FFu;  // bytes 1, 3
+  const uint32_t ev = w & 0x00FF00FFu;  // bytes 0, 2
+  const uint32_t od = pk_shr16(w, 8);    // bytes 1, 3 (one packed shift, nothing above them)
   float t[4] = {mix_lo(ev, cs24, cz), mix_lo(od, cs24, cz), mix_hi(ev, cs24, cz),
                 mix_hi(od, cs24, cz)};
 #pragma unroll
@@ -185,8 +185,8 @@ __device__ __forceinline__ void int8_decode16(const u32x4& w, float s24, float m
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t x = w[d] ^ 0x80808080u;
-    const uint32_t ev = x & 0x00FF00FFu;         // bytes 0, 2
-    const uint32_t od = (x >> 8) & 0x00FF00FFu;  // bytes 1, 3
+    const uint32_t ev = x & 0x00FF00FFu;  // bytes 0, 2
+    const uint32_t od = pk_shr16(x, 8);   // bytes 1, 3
     p[2 * d] = cvt_pk_bf16(mix_lo(ev, s24, m128s), mix_lo(od, s24, m128s));
     p[2 * d + 1] = cvt_pk_bf16(mix_hi(ev, s24, m128s), mix_hi(od, s24, m128s));
   }
@@ -224,7 +224,7 @@ __device__ __forceinline__ void ccq432_decode64(const uint32_t (&c)[6], float fi
   for (int d = 0; d < 6; ++d) {
 #pragma unroll
     for (int odd = 0; odd < 2; ++odd) {
-      const uint32_t x = odd ? ((c[d] >> 8) & 0x00FF00FFu) : (c[d] & 0x00FF00FFu);
+      const uint32_t x = odd ? pk_shr16(c[d], 8) : (c[d] & 0x00FF00FFu);
       const int b = 4 * d + odd;  // byte in the low half; b + 2 in the high half
       const uint32_t q0 = pk_shr16(x, 4);  // x < 256 per half: no bits above the state
       const uint32_t q1 = pk_shr16(x, 2) & 0x000F000Fu;
