@@ -1,0 +1,128 @@
+"""Parity at the full sizes of the benchmark workloads, through the same entry points and
+therefore the same kernel launches that bench.py times.
+
+The single-linear workloads compare every output against the oracle, with the weights
+quantized by the oracle's own quantizers from N(0, 0.02) draws (W4A16 512 x 512 RTN INT4 g64;
+WINT2 4096 x 4096 in both 2-bit formats).  The MoE layers (64 experts, hidden 8192, expert
+intermediate 3584, top-8) use seeded random packed bytes of the real layout and magnitudes --
+quantizing 5.6 G weights on the host would take too long -- drawn on the GPU by synth, copied
+back for the oracle, and compare sampled tokens: the oracle evaluates only the experts those
+tokens are routed to.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from wq_testutil import assert_close, to_device, to_host, torch_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+E, HIDDEN, INTER, TOPK = 64, 8192, 3584, 8
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import torch
+
+    import weight_only_bit_amd as wq
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wq.lib()
+    return wq
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_w4a16_512(wq, m):
+    import torch
+
+    _say(f"w4a16 512x512 m={m}")
+    w = synth.weights_f32((512, 512), 61, 1)
+    p = oracle.quantize(w, oracle.INT4, group=64)
+    x = synth.acts_bf16((m, 512), 61, 2, m)
+    ref = oracle.gemm(x, p)
+    y = wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), to_device(p))
+    assert_close(torch_bf16_bits(y), ref, f"w4a16 512x512 m={m}")
+
+
+@pytest.fixture(scope="module", params=["affine2", "ccq"])
+def wint2_4096(request):
+    fmt = {"affine2": oracle.AFFINE2, "ccq": oracle.CCQ}[request.param]
+    _say(f"quantizing 4096x4096 {request.param}")
+    w = synth.weights_f32((4096, 4096), 62, 1)
+    return request.param, oracle.quantize(w, fmt, group=64)
+
+
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_wint2_4096(wq, wint2_4096, m):
+    import torch
+
+    name, p = wint2_4096
+    _say(f"wint2 4096x4096 {name} m={m}")
+    x = synth.acts_bf16((m, 4096), 62, 2, m)
+    ref = oracle.gemm(x, p)
+    y = wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), to_device(p))
+    assert_close(torch_bf16_bits(y), ref, f"wint2 4096x4096 {name} m={m}")
+
+
+def _layer(wq, fmt, group, seed):
+    """One MoE layer of random packed weights on the GPU (gate, up, down)."""
+    mats = []
+    for j, (n, k) in enumerate(((INTER, HIDDEN), (INTER, HIDDEN), (HIDDEN, INTER))):
+        arr = synth.random_packed_device(fmt, E, n, k, seed + j, group=group)
+        mats.append(wq.PackedWeight(fmt, n, k, E, group,
+                                    *(arr.get(f) for f in ("codes", "scales", "zeros", "qscale",
+                                                            "super_scale", "code_scale",
+                                                            "code_zero")),
+                                    oracle.default_zp(fmt)))
+    return mats
+
+
+def _check_tokens(wq, mats, x, ids, wts, tokens, what):
+    import torch
+
+    y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(wts).cuda(), *mats)
+    got = torch_bf16_bits(y)[tokens]
+    _say(f"{what}: oracle on tokens {tokens.tolist()}")
+    host = [to_host(w) for w in mats]
+    ref = oracle.moe_ffn(x, ids, wts, *host, tokens=tokens)
+    assert_close(got, ref, what)
+
+
+@pytest.mark.parametrize("name", ["ccq", "int4pc"])
+def test_moe_decode_layer_full_size(wq, name):
+    # the decode step: 32 tokens, uniform top-8 of 64 experts (CCQ g64 layers and the stack's
+    # INT4 per-channel layers)
+    fmt, group = (oracle.CCQ, 64) if name == "ccq" else (oracle.INT4, 0)
+    _say(f"moe decode full size {name}")
+    mats = _layer(wq, fmt, group, 6300 + fmt)
+    x = synth.acts_bf16((32, HIDDEN), 63, 1)
+    ids, wts = synth.routing_uniform(32, TOPK, E, 63, 2)
+    _check_tokens(wq, mats, x, ids, wts, np.array([0, 17, 31], np.int32),
+                  f"moe decode full size {name}")
+
+
+def test_moe_prefill_layer_full_size(wq):
+    # the prefill layer: 4096 tokens, Zipf-skewed top-8 of 64 experts, CCQ g64; sampled tokens
+    # routed to the heaviest expert, to the lightest expert that has rows, and the last token
+    _say("moe prefill full size ccq")
+    mats = _layer(wq, oracle.CCQ, 64, 6400)
+    T = 4096
+    x = synth.acts_bf16((T, HIDDEN), 64, 1)
+    ids, wts = synth.routing_zipf(T, TOPK, E, 64, 2)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    heavy = int(np.argmax(counts))
+    light = int(np.argmin(np.where(counts > 0, counts, T * TOPK)))
+    assert counts[heavy] > 1024 and counts[light] < 64
+    t_heavy = int(np.nonzero((ids == heavy).any(axis=1))[0][0])
+    t_light = int(np.nonzero((ids == light).any(axis=1))[0][-1])
+    tokens = np.array(sorted({t_heavy, t_light, T - 1}), np.int32)
+    _check_tokens(wq, mats, x, ids, wts, tokens, "moe prefill full size ccq")

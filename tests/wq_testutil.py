@@ -52,3 +52,18 @@ def assert_close(y_gpu_bits, y_ref_bits, what=""):
             f"{what}: {int(bad.sum())}/{bad.size} outside tolerance; worst at {np.unravel_index(i, g.shape)} "
             f"gpu={g.flat[i]:.6g} ref={r.flat[i]:.6g} rms={rms:.4g}")
     return float((err / (np.abs(r) + rms + 1e-300)).max()) if r.size else 0.0
+
+
+def to_host(w):
+    """weight_only_bit_amd.PackedWeight -> oracle.Packed (host copies of the same bytes)."""
+    import oracle
+
+    def h(t):
+        if t is None:
+            return None
+        a = t.cpu().numpy()
+        return a.view(np.uint16) if a.dtype == np.int16 else a
+
+    return oracle.Packed(w.format, w.n, w.k, w.experts, w.group, h(w.codes), h(w.scales),
+                         h(w.zeros), h(w.qscale), h(w.super_scale), h(w.code_scale),
+                         h(w.code_zero), w.zp)
