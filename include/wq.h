@@ -196,7 +196,7 @@ wq_status wq_quantize_ccq(const float* w, int64_t n, int64_t k, int32_t zp, int3
  *   out must hold (n+1)/2 bytes; WQ_ERR_RANGE (nothing written) for a code outside -8..7.
  * wq_unpack_int4: the first n codes, sign-extended; data holds at least (n+1)/2 bytes.
  * wq_packed_size: nominal bytes of n_codes codes of `bits` bits (n*bits/8, rounded up);
- *   -1 for negative n or bits outside 1..32. */
+ *   -1 for negative n, bits outside 1..32, or a bit count n*bits beyond int64. */
 wq_status wq_pack_int4(const int32_t* codes, int64_t n, uint8_t* out);
 wq_status wq_unpack_int4(const uint8_t* data, int64_t n, int32_t* out);
 int64_t wq_packed_size(int64_t n_codes, int32_t bits);

@@ -50,6 +50,10 @@ def test_pack_helpers_match_printed_values(wq):
     assert wq.wq_packed_size(7_000_000_000, 16) == 14_000_000_000
     assert wq.wq_packed_size(3, 4) == 2
     assert wq.wq_packed_size(-1, 4) == -1
+    big = (2**63 - 1 - 7) // 32  # the largest count whose bit count fits int64 at 32 bits
+    assert wq.wq_packed_size(big, 32) == (big * 32 + 7) // 8
+    assert wq.wq_packed_size(big + 1, 32) == -1
+    assert wq.wq_packed_size(2**62, 4) == -1
     for bad in ([8], [-9]):
         with pytest.raises(ValueError, match="WQ_ERR_RANGE"):
             wq.wq_pack_int4(bad)

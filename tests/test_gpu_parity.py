@@ -159,6 +159,23 @@ def test_gemm_parity(wq, name, nk, m):
     assert_close(torch_bf16_bits(y), ref, f"gemm {name} {n}x{k} m={m}")
 
 
+def test_gemm_row_chunks(wq):
+    # Group-64 INT8 runs the decode-streaming kernel for every row count; past 65535 blocks of
+    # 32 rows the product is split into several launches.  Rows on both sides of the split.
+    import torch
+
+    n, k = 32, 64
+    chunk = 65535 * 32
+    m = chunk + 77
+    _say(f"gemm row chunks int8 m={m}")
+    p = _quant(oracle.INT8, (n, k), (7, 1), group=64)
+    x = synth.acts_bf16((m, k), 7, 2)
+    y = wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), to_device(p))
+    rows = np.array([0, 1, chunk - 1, chunk, chunk + 1, m - 1])
+    ref = oracle.gemm(np.ascontiguousarray(x[rows]), p)
+    assert_close(torch_bf16_bits(y)[rows], ref, "gemm row chunks")
+
+
 def test_gemm_deterministic(wq):
     import torch
 

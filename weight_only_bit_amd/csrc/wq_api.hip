@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -169,6 +170,8 @@ constexpr int32_t kMaxExperts = 512;
 constexpr int64_t kSkinnyMaxRows = 32;
 // MoE layers whose experts average at least this many routed rows use the tiled kernels.
 constexpr double kMoeTiledRows = 32.0;
+// Largest grid z extent one launch uses.
+constexpr int64_t kMaxGridZ = 65535;
 
 }  // namespace
 
@@ -213,6 +216,7 @@ wq_status wq_unpack_int4(const uint8_t* data, int64_t n, int32_t* out) {
 
 int64_t wq_packed_size(int64_t n_codes, int32_t bits) {
   if (n_codes < 0 || bits < 1 || bits > 32) return -1;
+  if (n_codes > (INT64_MAX - 7) / bits) return -1;  // the bit count would overflow
   return (n_codes * (int64_t)bits + 7) / 8;
 }
 
@@ -283,9 +287,20 @@ wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y,
   const int64_t n_tiles = (w->n + 15) / 16;
   // Split K across the 4 waves when 4-tile workgroups would leave the 256 CUs idle.
   const int ksplit = (n_tiles / 4 < 512 && w->k % 256 == 0) ? 4 : 1;
-  return hip_status(wq::launch_skinny(w->format, wq::MODE_DENSE, mt, ksplit, a, 1,
-                                      (m + rows - 1) / rows, s),
+  // One launch covers at most kMaxGridZ row blocks (the grid's z extent); more rows (group-64
+  // INT8 runs this kernel for every row count) take further launches on the same stream.
+  const int64_t chunk = kMaxGridZ * rows;
+  for (int64_t r0 = 0; r0 < m; r0 += chunk) {
+    const int64_t mr = m - r0 < chunk ? m - r0 : chunk;
+    a.a = x + r0 * w->k;
+    a.out = y + r0 * w->n;
+    a.M = mr;
+    st = hip_status(wq::launch_skinny(w->format, wq::MODE_DENSE, mt, ksplit, a, 1,
+                                      (mr + rows - 1) / rows, s),
                     "wq_gemm launch");
+    if (st != WQ_OK) return st;
+  }
+  return WQ_OK;
 }
 
 size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t hidden,

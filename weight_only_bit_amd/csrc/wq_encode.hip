@@ -254,13 +254,9 @@ hipError_t launch_ccq_encode(const float* w, int64_t n, int64_t k, int32_t zp, b
                              float* code_scale, float* code_zero, hipStream_t stream) {
   const size_t lds = ccq_encode_lds_bytes(k);
   auto kern = refine ? ccq_encode_kernel<true> : ccq_encode_kernel<false>;
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[refine]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set[refine] = true;
-  }
+  static std::atomic<uint64_t> lds_set[2];  // per variant, one bit per device
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), 160 * 1024, lds_set[refine]);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)n), dim3(ENC_THREADS), lds, stream, w, k, zp, codes,
                      qscale, super_scale, code_scale, code_zero);
   return hipGetLastError();

@@ -4,9 +4,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "wq_device.hpp"
 
 namespace wq {
+
+// Raise a kernel's dynamic-LDS limit on the current device, once per device: the attribute is
+// per-device state, and `done` holds one bit per device already set (ids below 64; higher ids
+// set it on every call).  Safe to call from several host threads.
+inline hipError_t ensure_dynamic_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Arguments of the decode-streaming ("skinny") MFMA kernels.
 struct SkinnyArgs {

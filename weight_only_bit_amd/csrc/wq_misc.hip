@@ -260,14 +260,11 @@ hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int
   const int T = route_threads(experts);
   const int S = T >= experts ? T / experts : 1;
   const size_t lds = sizeof(int32_t) * ((size_t)T * experts + (size_t)S * experts + experts);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(sizeof(int32_t) * (ROUTE_LDS_COUNTERS + 2 * 1024 + 512)));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&route_kernel),
+                                    (int)(sizeof(int32_t) * (ROUTE_LDS_COUNTERS + 2 * 1024 + 512)),
+                                    lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_kernel, dim3(1), dim3(T), lds, stream, ids, npairs, experts, offsets,
                      sorted_pairs);
   return hipGetLastError();

@@ -469,14 +469,10 @@ hipError_t launch_one(const SkinnyArgs& a, int64_t gy, int64_t gz, hipStream_t s
   constexpr int KCT = chunk_cols<FMT, KSPLIT>() * KSPLIT;
   constexpr size_t lds_bytes = 2 * (size_t)(MT * 16) * (KCT * 2 + 16);
   constexpr int TPW = (KSPLIT == 4) ? 1 : (MODE == MODE_GATEUP ? 2 : 4);
-  static bool attr_set = false;  // per instantiation; the attribute is per-function state
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, MODE, KSPLIT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // per instantiation, one bit per device
+  hipError_t e = ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, MODE, KSPLIT>), (int)lds_bytes, lds_set);
+  if (e != hipSuccess) return e;
   const int64_t ntiles = (a.N + 15) / 16;
   dim3 grid((unsigned)((ntiles + TPW - 1) / TPW), (unsigned)gy, (unsigned)gz);
   hipLaunchKernelGGL((skinny_kernel<FMT, MT, MODE, KSPLIT>), grid, dim3(256), lds_bytes, s, a);
