@@ -137,6 +137,7 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, f
 #pragma unroll
   for (int b = 0; b < 4; ++b)
     if (CLAMP) t[b] = __builtin_amdgcn_fmed3f(t[b], 0.0f, 32767.0f);
+  float r[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     // P = C of byte 2h (low half) | C of byte 2h + 1 (high half): the magic-number add of
@@ -152,11 +153,17 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, f
     const uint32_t q1 = pk_shr16(P, 6) & 0x003F003Fu;
     const uint32_t q2 = pk_shr16(P, 3) & 0x003F003Fu;
     const uint32_t q3 = P & 0x003F003Fu;
-    p[4 * h + 0] = cvt_pk_bf16(mix_lo(q0, s24, mzs), mix_lo(q1, s24, mzs));
-    p[4 * h + 1] = cvt_pk_bf16(mix_lo(q2, s24, mzs), mix_lo(q3, s24, mzs));
-    p[4 * h + 2] = cvt_pk_bf16(mix_hi(q0, s24, mzs), mix_hi(q1, s24, mzs));
-    p[4 * h + 3] = cvt_pk_bf16(mix_hi(q2, s24, mzs), mix_hi(q3, s24, mzs));
+    r[8 * h + 0] = mix_lo(q0, s24, mzs);
+    r[8 * h + 1] = mix_lo(q1, s24, mzs);
+    r[8 * h + 2] = mix_lo(q2, s24, mzs);
+    r[8 * h + 3] = mix_lo(q3, s24, mzs);
+    r[8 * h + 4] = mix_hi(q0, s24, mzs);
+    r[8 * h + 5] = mix_hi(q1, s24, mzs);
+    r[8 * h + 6] = mix_hi(q2, s24, mzs);
+    r[8 * h + 7] = mix_hi(q3, s24, mzs);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = cvt_pk_bf16(r[2 * i], r[2 * i + 1]);
 }
 
 // INT4: two dwords = 16 signed nibbles (first weight in the low nibble).  XOR 8 biases a
@@ -164,32 +171,39 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, f
 // s24 = s * 2^24, m8s = -8 s.
 __device__ __forceinline__ void int4_decode16(uint32_t w0, uint32_t w1, float s24, float m8s,
                                               uint32_t (&p)[8]) {
+  float r[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t d = (h ? w1 : w0) ^ 0x88888888u;  // halves: nibbles 0..3 and 4..7
-    const uint32_t q0 = d & 0x000F000Fu;
-    const uint32_t q1 = pk_shr16(d, 4) & 0x000F000Fu;
-    const uint32_t q2 = pk_shr16(d, 8) & 0x000F000Fu;
-    const uint32_t q3 = pk_shr16(d, 12);
-    p[4 * h + 0] = cvt_pk_bf16(mix_lo(q0, s24, m8s), mix_lo(q1, s24, m8s));
-    p[4 * h + 1] = cvt_pk_bf16(mix_lo(q2, s24, m8s), mix_lo(q3, s24, m8s));
-    p[4 * h + 2] = cvt_pk_bf16(mix_hi(q0, s24, m8s), mix_hi(q1, s24, m8s));
-    p[4 * h + 3] = cvt_pk_bf16(mix_hi(q2, s24, m8s), mix_hi(q3, s24, m8s));
+    const uint32_t q[4] = {d & 0x000F000Fu, pk_shr16(d, 4) & 0x000F000Fu,
+                           pk_shr16(d, 8) & 0x000F000Fu, pk_shr16(d, 12)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[8 * h + i] = mix_lo(q[i], s24, m8s);
+      r[8 * h + 4 + i] = mix_hi(q[i], s24, m8s);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = cvt_pk_bf16(r[2 * i], r[2 * i + 1]);
 }
 
 // INT8: 16 signed bytes (k order).  XOR 0x80 biases a byte q to q + 128 in 0..255 (< 1024, so
 // an f16 subnormal), value = fl((q + 128) s - 128 s); s24 = s * 2^24, m128s = -128 s.
 __device__ __forceinline__ void int8_decode16(const u32x4& w, float s24, float m128s,
                                               uint32_t (&p)[8]) {
+  float r[16];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t x = w[d] ^ 0x80808080u;
     const uint32_t ev = x & 0x00FF00FFu;  // bytes 0, 2
     const uint32_t od = pk_shr16(x, 8);   // bytes 1, 3
-    p[2 * d] = cvt_pk_bf16(mix_lo(ev, s24, m128s), mix_lo(od, s24, m128s));
-    p[2 * d + 1] = cvt_pk_bf16(mix_hi(ev, s24, m128s), mix_hi(od, s24, m128s));
+    r[4 * d + 0] = mix_lo(ev, s24, m128s);
+    r[4 * d + 1] = mix_lo(od, s24, m128s);
+    r[4 * d + 2] = mix_hi(ev, s24, m128s);
+    r[4 * d + 3] = mix_hi(od, s24, m128s);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = cvt_pk_bf16(r[2 * i], r[2 * i + 1]);
 }
 
 // 2-bit affine: one dword = 16 codes (first in the lowest two bits); value = fl(q s - z s)
@@ -200,11 +214,14 @@ __device__ __forceinline__ void affine2_decode16(uint32_t w, float s24, float mz
 #pragma unroll
   for (int i = 0; i < 7; ++i) q[i] = pk_shr16(w, (uint16_t)(2 * i)) & 0x00030003u;
   q[7] = pk_shr16(w, 14);
+  float r[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    p[j] = cvt_pk_bf16(mix_lo(q[2 * j], s24, mzs), mix_lo(q[2 * j + 1], s24, mzs));
-    p[4 + j] = cvt_pk_bf16(mix_hi(q[2 * j], s24, mzs), mix_hi(q[2 * j + 1], s24, mzs));
+  for (int i = 0; i < 8; ++i) {
+    r[i] = mix_lo(q[i], s24, mzs);
+    r[8 + i] = mix_hi(q[i], s24, mzs);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = cvt_pk_bf16(r[2 * j], r[2 * j + 1]);
 }
 
 // CCQ without code cluster ("CCQ", section 3.5, "Dequantization without Code Cluster"): one
