@@ -229,7 +229,9 @@ def main():
         from wq_testutil import assert_close, torch_bf16_bits
 
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        sample_layers = [n4] + ([0] if n4 > 0 else [])
+        # up to three of the 2-bit-class layers and two INT4 per-channel layers: ~10 s of oracle
+        # work on 16 host cores (each layer's touched experts are decoded and multiplied)
+        sample_layers = [l for l in (n4, n4 + 1, n4 + 2) if l < L] + [l for l in (0, 1) if l < n4]
         tot_bytes, tot_s, errs = 0, 0.0, []
         for l in sample_layers:
             g, u, dn = (to_host_packed(oracle, w) for w in layers[l])
