@@ -127,7 +127,8 @@ wq_status wq_dequantize(const wq_weight* w, uint16_t* out, void* stream);
  * and fp32 accumulation (FastDeploy "WINT2 Quantization"; the pages' GEMV and grouped-GEMM
  * operator benchmarks).  x bf16 [m][k], y bf16 [m][n], w->experts must be 1.  m == 0 is a
  * no-op.  Small m (<= 32) runs the decode kernels that stream the packed weights once;
- * larger m runs the MFMA kernel with LDS-staged dequantized tiles. */
+ * larger m runs the MFMA kernel with LDS-staged dequantized tiles, except group-64 INT8,
+ * which runs the decode kernels at every m (in launches of at most 65535 x 32 rows). */
 wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y, void* stream);
 
 /* Bytes of device workspace wq_moe_route / wq_moe_ffn need for t tokens, top-k routing over
@@ -138,7 +139,9 @@ size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t 
 /* Group the (token, slot) pairs p = t*topk + j by expert (sort by expert id, stable in p):
  * expert_offsets[e] = number of pairs routed to experts < e (expert_offsets[experts] =
  * t*topk); sorted_pairs[expert_offsets[e] ...] lists expert e's pairs in increasing p.
- * topk_ids int32 [t][topk] must lie in [0, experts) (not checked on the device). */
+ * topk_ids int32 [t][topk] must lie in [0, experts); the device drops a pair whose id lies
+ * outside (it lands in no expert's list and nothing is written out of bounds), and the
+ * outputs of its token are then unspecified. */
 wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t experts,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* ws,
                        size_t ws_bytes, void* stream);
