@@ -308,6 +308,37 @@ def test_moe_ffn_parity(wq, case):
     assert_close(torch_bf16_bits(y), ref, f"moe {case}")
 
 
+def test_empty_inputs(wq):
+    # no rows, no tokens: nothing to compute, no error, empty outputs
+    import torch
+
+    p = _quant(oracle.CCQ, (64, 128), (8, 1))
+    y = wq.wq_gemm(torch.zeros((0, 128), dtype=torch.int16).cuda(), to_device(p))
+    assert tuple(y.shape) == (0, 64)
+    gate = _quant(oracle.CCQ, (4, 64, 128), (8, 2))
+    up = _quant(oracle.CCQ, (4, 64, 128), (8, 3))
+    down = _quant(oracle.CCQ, (4, 128, 64), (8, 4))
+    ym = wq.wq_moe_ffn(torch.zeros((0, 128), dtype=torch.int16).cuda(),
+                       torch.zeros((0, 2), dtype=torch.int32).cuda(),
+                       torch.zeros((0, 2), dtype=torch.float32).cuda(),
+                       to_device(gate), to_device(up), to_device(down))
+    torch.cuda.synchronize()
+    assert tuple(ym.shape) == (0, 128)
+
+
+@pytest.mark.parametrize("name", ["int4", "ccq", "int8pc"])
+@pytest.mark.parametrize("m", [8, 300])
+def test_zero_activations_give_plus_zero(wq, name, m):
+    # a zero activation row gives exactly +0 in every output (sums start at +0 and add +0 / -0
+    # products), in both the decode-streaming and the tiled kernels
+    import torch
+
+    fmt, group = _fmt_group(name)
+    p = _quant(fmt, (96, 256), (8, 5, fmt), group=group)
+    y = wq.wq_gemm(torch.zeros((m, 256), dtype=torch.int16).cuda(), to_device(p))
+    assert np.all(torch_bf16_bits(y) == 0)
+
+
 def test_moe_all_tokens_one_expert(wq):
     # every token routed to experts 0 and 1: a 40-row expert exercises two row super-tiles
     import torch
