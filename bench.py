@@ -75,12 +75,13 @@ def parse():
                          "2.75 bpw; ccqh = hybrid (3,3,2)+(3,4,2), 2.5 bpw")
     ap.add_argument("--workload", default="moe_stack_decode",
                     choices=["moe_stack_decode", "moe_prefill", "dense_decode", "copy_calibration",
-                             "pages_shapes", "ccq_encode"],
+                             "pages_shapes", "ccq_encode", "hbm_achievable"],
                     help="moe_stack_decode (default): the 54-layer stack step; moe_prefill: one "
                          "CCQ MoE layer at 4096 tokens with Zipf-skewed routing; dense_decode: "
                          "one 4096x4096 CCQ / 2-bit affine linear at 1, 8, 32 rows; pages_shapes: "
                          "the GEMV and grouped-GEMM shapes of the CCQ paper's operator tables; "
-                         "ccq_encode: the GPU CCQ encoder on one expert gate tensor")
+                         "ccq_encode: the GPU CCQ encoder on one expert gate tensor; "
+                         "hbm_achievable: torch's read-only reduction and copy bandwidth (context)")
     return ap.parse_args()
 
 
@@ -128,6 +129,8 @@ def main():
         return pages_shapes(args)
     if args.workload == "ccq_encode":
         return ccq_encode(args)
+    if args.workload == "hbm_achievable":
+        return hbm_achievable(args)
 
     import numpy as np
     import torch
@@ -593,6 +596,35 @@ def copy_calibration(args):
     torch.cuda.synchronize()
     print(json.dumps({"workload": "copy_calibration", "bytes_read": n, "bytes_written": n,
                       "copies": max(args.steps, 1)}), flush=True)
+
+
+def hbm_achievable(args):
+    """Context for the HBM fractions: what plain library kernels (torch) reach on this GPU --
+    a read-only reduction over 4 GiB of bf16 and a 2 GiB device-to-device copy, timed with
+    events over repeated calls.  Not part of the path."""
+    import torch
+
+    torch.cuda.set_device(0)
+    out = {"workload": "hbm_achievable", "unit": "GB/s"}
+    x = torch.ones(2 << 30, dtype=torch.bfloat16, device="cuda:0")  # 4 GiB
+    src = torch.ones(2 << 30, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for name, fn, nbytes in (("read_reduce", lambda: x.sum(dtype=torch.float32), x.numel() * 2),
+                             ("copy", lambda: dst.copy_(src), 2 * src.numel())):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(args.steps, 5)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    out["hbm_peak"] = HBM_PEAK_GBS
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
