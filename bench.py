@@ -371,6 +371,44 @@ def moe_prefill(args):
     print(json.dumps(out), flush=True)
 
 
+def graph_us(fn, calls, replays=3):
+    """Mean GPU time per call of fn(i), i = 0 .. calls-1, with no host launch cost: the calls are
+    captured once in a HIP graph (after eager warm-up calls) and the graph is replayed.  Also
+    returns the same calls' mean when launched eagerly one by one from Python."""
+    import torch
+
+    for i in range(min(calls, 4)):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(calls):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) / calls * 1e3
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (replays * calls) * 1e3
+    del g
+    return us, eager
+
+
 def dense_decode(args):
     """One 4096 x 4096 linear at 1, 8 and 32 rows, CCQ, 2-bit affine and WINT8 (per channel, the
     deployment's dense layers); each call reads one of
@@ -401,22 +439,16 @@ def dense_decode(args):
         for m in (1, 8, 32):
             x = torch.from_numpy(synth.acts_bf16((m, Kd), 502, m).view(np.int16)).to(dev)
             y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
-            for i in range(len(copies)):
-                wq.wq_gemm(x, copies[i], y=y)
-            torch.cuda.synchronize()
-            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = max(args.steps, 1) * len(copies)
-            st.record()
-            for i in range(reps):
-                wq.wq_gemm(x, copies[i % len(copies)], y=y)
-            en.record()
-            torch.cuda.synchronize()
-            us = st.elapsed_time(en) / reps * 1e3
-            res[f"{name}_m{m}"] = {"us": round(us, 2), "GB/s": round(one / (us * 1e-6) / 1e9, 1)}
+            us, eager = graph_us(lambda i: wq.wq_gemm(x, copies[i % len(copies)], y=y), len(copies),
+                                 max(args.steps, 1))
+            res[f"{name}_m{m}"] = {"us": round(us, 2), "GB/s": round(one / (us * 1e-6) / 1e9, 1),
+                                   "eager_us": round(eager, 2)}
     out = {"metric": "weight-stream GB/s, dense 4096x4096 linear", "value": res["ccq_m1"]["GB/s"],
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "dense_decode", "n": N, "k": Kd}, "results": res}
+           "config": {"workload": "dense_decode", "n": N, "k": Kd}, "results": res,
+           "note": "us: per call from HIP-graph replay of the calls (no host launch cost); "
+                   "eager_us: the same calls launched one by one from Python"}
     print(json.dumps(out), flush=True)
 
 
@@ -452,16 +484,8 @@ def pages_shapes(args):
     dev = torch.device("cuda:0")
     fields = ("codes", "scales", "zeros", "qscale", "super_scale", "code_scale", "code_zero")
 
-    def timed(fn, reps):
-        fn(0)
-        torch.cuda.synchronize()
-        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st.record()
-        for i in range(reps):
-            fn(i)
-        en.record()
-        torch.cuda.synchronize()
-        return st.elapsed_time(en) / reps * 1e3  # us
+    def timed(fn, calls):
+        return graph_us(fn, calls, max(args.steps, 1))[0]  # us per call, graph replay
 
     gemv = {}
     for (k, n, m), (ms_w2, ms_ccq) in PAGES_GEMV_MS.items():
@@ -475,7 +499,7 @@ def pages_shapes(args):
                     break
             x = torch.from_numpy(synth.acts_bf16((m, k), 701, m, k).view(np.int16)).to(dev)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-            us = timed(lambda i: wq.wq_gemm(x, copies[i % len(copies)], y=y), max(args.steps, 1) * len(copies))
+            us = timed(lambda i: wq.wq_gemm(x, copies[i % len(copies)], y=y), len(copies))
             row[name] = {"us": round(us, 2), "GB/s": round(copies[0].nbytes() / (us * 1e-6) / 1e9, 1)}
             del copies
         row["pages_h20_ms"] = {"wint2_standard": ms_w2, "ccq": ms_ccq}
@@ -502,7 +526,7 @@ def pages_shapes(args):
                 routes.append((off, pairs, len(np.unique(ids))))
             h = torch.empty((m * topk, 512), dtype=torch.bfloat16, device=dev)
             d = torch.empty((m * topk, 7168), dtype=torch.float32, device=dev)
-            reps = max(args.steps, 1) * len(routes)
+            reps = len(routes)
             us_gu = timed(lambda i: wq.wq_moe_gate_up(x, routes[i % 64][0], routes[i % 64][1], topk, gw, uw, h=h), reps)
             us_dn = timed(lambda i: wq.wq_moe_down(h, m, topk, routes[i % 64][0], routes[i % 64][1], dw, d=d), reps)
             touched = float(np.mean([r[2] for r in routes]))
@@ -520,7 +544,8 @@ def pages_shapes(args):
     out = {"metric": "latency of the pages' operator shapes (us)", "value": gemv["4096x4096_m1"]["ccq"]["us"],
            "unit": "us", "n_gpus": 1, "steps": args.steps, "higher_is_better": False, "dtype": "bf16",
            "data": "synthetic", "config": {"workload": "pages_shapes"}, "gemv": gemv, "grouped_gemm": grouped,
-           "note": "pages_h20_ms are the pages' own H20 timings, context only"}
+           "note": "us per call from HIP-graph replay (no host launch cost); pages_h20_ms are the "
+                   "pages' own H20 timings, context only"}
     print(json.dumps(out), flush=True)
 
 
