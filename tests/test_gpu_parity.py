@@ -159,6 +159,51 @@ def test_gemm_parity(wq, name, nk, m):
     assert_close(torch_bf16_bits(y), ref, f"gemm {name} {n}x{k} m={m}")
 
 
+# Few rows whose activations fit in LDS whole (rows x (2 K + 16) + 128 bytes <= 132 KiB, K a
+# multiple of 256) take the single-staging kernel: 4 waves split K, or 16 when the output tiles
+# are few and K % 1024 == 0.  K = 8448 (4 waves) gives each wave 2112 columns and K = 17408 (16
+# waves) 1088: more steps than a lane holds at once for every format, and a last step that runs
+# past the wave's part.  m = 8 at K = 8448 and m = 4 at K = 17408 just miss the LDS limit and
+# take the chunked kernel; m = 7 and m = 16 stage in two rounds; n = 40 leaves a partial tile.
+GEMV_CASES = [(40, 8448, 1), (40, 8448, 3), (40, 8448, 7), (40, 8448, 8), (200, 2048, 16),
+              (24, 768, 5), (40, 17408, 1), (40, 17408, 3), (40, 17408, 4), (64, 4096, 16)]
+
+
+@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("case", GEMV_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_gemv_path_parity(wq, name, case):
+    import torch
+
+    fmt, group = _fmt_group(name)
+    n, k, m = case
+    _say(f"gemv {name} n={n} k={k} m={m}")
+    p = _quant(fmt, (n, k), (41, fmt, group, n, k), group=group)
+    x = synth.acts_bf16((m, k), 42, m, k)
+    ref = oracle.gemm(x, p)
+    y = wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), to_device(p))
+    assert_close(torch_bf16_bits(y), ref, f"gemv {name} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("k", [768, 1024])
+def test_gemv_decodes_every_weight_bit_exact(wq, name, k):
+    # The identity-activation check of the decode, 16 rows at a time (single-staging kernel):
+    # k = 768 gives each of 4 waves 192 columns (CCQ lanes 2 and 3 and INT4's second step run
+    # past the part and must read zeros); k = 1024 gives each of 16 waves 64 columns.
+    import torch
+
+    fmt, group = _fmt_group(name)
+    n = 40
+    p = _quant(fmt, (n, k), (43, fmt, group), group=group)
+    ref = oracle.dequantize(p)
+    d = to_device(p)
+    for c0 in range(0, k, 16):
+        x = np.zeros((16, k), np.uint16)
+        x[np.arange(16), c0 + np.arange(16)] = 0x3F80
+        y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d))
+        assert np.array_equal(y.T, _product_bits(ref[:, c0:c0 + 16])), f"columns {c0}..{c0 + 15}"
+
+
 def test_gemm_row_chunks(wq):
     # Group-64 INT8 runs the decode-streaming kernel for every row count; past 65535 blocks of
     # 32 rows the product is split into several launches.  Rows on both sides of the split.

@@ -287,6 +287,9 @@ wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y,
   const int64_t n_tiles = (w->n + 15) / 16;
   // Split K across the 4 waves when 4-tile workgroups would leave the 256 CUs idle.
   const int ksplit = (n_tiles / 4 < 512 && w->k % 256 == 0) ? 4 : 1;
+  // Few rows whose activations fit in LDS whole: the single-staging kernel (lower latency).
+  if (ksplit == 4 && wq::gemv_fits(m, w->n, w->k))
+    return hip_status(wq::launch_gemv(w->format, a, s), "wq_gemm launch");
   // One launch covers at most kMaxGridZ row blocks (the grid's z extent); more rows (group-64
   // INT8 runs this kernel for every row count) take further launches on the same stream.
   const int64_t chunk = kMaxGridZ * rows;

@@ -47,6 +47,11 @@ enum { MODE_DENSE = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
 hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
                          int64_t grid_y, int64_t grid_z, hipStream_t stream);
 
+// Dense products of 1..16 activation rows whose rows fit in LDS whole (rows x (2 K + 16) bytes
+// plus 128 at most 132 KiB) with K % 256 == 0: one launch, the waves of a workgroup split K.
+bool gemv_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemv(int fmt, const SkinnyArgs& args, hipStream_t stream);
+
 hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t* out,
                           hipStream_t stream);
 

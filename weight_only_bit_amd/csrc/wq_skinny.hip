@@ -167,6 +167,91 @@ __device__ __forceinline__ void load_raw(Raw<FMT>& r, const WaveW<FMT>& v, int32
   }
 }
 
+// One step of one lane: decode its packed data rw (WPL weights of its row) into B fragments and
+// multiply them with the A fragments at abase (LDS: the lane's activation row at the step's
+// first column of this lane; tile t of 16 rows at abase + t * tpitch) into acc.
+template <int FMT, int MT, bool CLAMP>
+__device__ __forceinline__ void step_mma(const Raw<FMT>& rw, const WaveW<FMT>& W, float cs24,
+                                         float fin24, float mzp24, const uint8_t* abase,
+                                         int tpitch, f32x4 (&acc)[MT]) {
+  constexpr int WPL = lane_weights<FMT>();
+  if constexpr (is_alg2(FMT)) {
+    uint32_t p[32];
+    if constexpr (FMT == FMT_CCQ432) {
+      // shift the window so that the group starts at byte 0
+      const uint32_t w6[6] = {rw.codes[0], rw.codes[1], rw.codes[2], rw.codes[3],
+                              rw.extra.x, rw.extra.y};
+      uint32_t c[6];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) c[i] = __builtin_amdgcn_alignbit(w6[i + 1], w6[i], W.qshift);
+      c[5] = w6[5] >> W.qshift;
+      ccq432_decode64(c, fin24, mzp24, p);
+    } else {
+      const uint32_t c[5] = {rw.codes[0], rw.codes[1], rw.codes[2], rw.codes[3], rw.extra.x};
+      ccqh_decode64(c, fin24, mzp24, p);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 B0 = {p[8 * q], p[8 * q + 1], p[8 * q + 2], p[8 * q + 3]};
+      const u32x4 B1 = {p[8 * q + 4], p[8 * q + 5], p[8 * q + 6], p[8 * q + 7]};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const u32x4 A0 = *reinterpret_cast<const u32x4*>(abase + t * tpitch + q * 32);
+        const u32x4 A1 =
+            *reinterpret_cast<const u32x4*>(abase + t * tpitch + q * 32 + 16);
+        acc[t] = mfma16x16x32(A0, B0, acc[t]);
+        acc[t] = mfma16x16x32(A1, B1, acc[t]);
+      }
+    }
+    return;
+  }
+  // s24 = s * 2^24 (the decode helpers' scaled form), mzs = -z * s
+  float s24 = 0.0f, mzs = 0.0f;
+  if constexpr (FMT == FMT_CCQ2) {
+    s24 = (float)((rw.scale >> W.qshift) & 0xFu) * fin24;  // = fl(s_q * super) * 2^24
+    mzs = s24 * mzp24;
+  } else if constexpr (FMT == FMT_INT4) {
+    s24 = bf16_bits_to_f32(rw.scale & 0xFFFFu) * kTwo24;
+    mzs = s24 * (-8.0f / kTwo24);
+  } else if constexpr (FMT == FMT_INT4PC) {
+    s24 = fin24;
+    mzs = fin24 * (-8.0f / kTwo24);
+  } else if constexpr (FMT == FMT_INT8) {
+    s24 = bf16_bits_to_f32(rw.scale & 0xFFFFu) * kTwo24;
+    mzs = s24 * (-128.0f / kTwo24);
+  } else if constexpr (FMT == FMT_INT8PC) {
+    s24 = fin24;
+    mzs = fin24 * (-128.0f / kTwo24);
+  } else {
+    const float s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
+    s24 = s * kTwo24;
+    mzs = -(float)(rw.zero & 0xFFu) * s;
+  }
+  // 16 weights (two MFMAs) at a time
+#pragma unroll
+  for (int q = 0; q < WPL / 16; ++q) {
+    uint32_t p[8];
+    if constexpr (FMT == FMT_CCQ2) {
+      ccq_decode16<CLAMP>(rw.codes[q], cs24, W.cz, s24, mzs, p);
+    } else if constexpr (is_int4(FMT)) {
+      int4_decode16(rw.codes[2 * q], rw.codes[2 * q + 1], s24, mzs, p);
+    } else if constexpr (is_int8(FMT)) {
+      int8_decode16(rw.codes, s24, mzs, p);
+    } else {
+      affine2_decode16(rw.codes[q], s24, mzs, p);
+    }
+    const u32x4 B0 = {p[0], p[1], p[2], p[3]};
+    const u32x4 B1 = {p[4], p[5], p[6], p[7]};
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const u32x4 A0 = *reinterpret_cast<const u32x4*>(abase + t * tpitch + q * 32);
+      const u32x4 A1 = *reinterpret_cast<const u32x4*>(abase + t * tpitch + q * 32 + 16);
+      acc[t] = mfma16x16x32(A0, B0, acc[t]);
+      acc[t] = mfma16x16x32(A1, B1, acc[t]);
+    }
+  }
+}
+
 template <int FMT, int MT, int MODE, int KSPLIT>
 __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   constexpr int WPL = lane_weights<FMT>();     // weights per lane per step
@@ -297,84 +382,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
 #pragma unroll
       for (int j = 0; j < SPC; ++j) {
         if (c * KCW + j * SSK >= Kpp) break;
-        const Raw<FMT>& rw = r[j];
         // lane's A fragments: row t*16 + nl, columns kw*KCW + j*SSK + kb*WPL + 8h
-        const uint8_t* abase = &lds[buf][nl * PITCH + (kw * KCW + j * SSK + kb * WPL) * 2];
-        if constexpr (is_alg2(FMT)) {
-          uint32_t p[32];
-          if constexpr (FMT == FMT_CCQ432) {
-            // shift the window so that the group starts at byte 0
-            const uint32_t w6[6] = {rw.codes[0], rw.codes[1], rw.codes[2], rw.codes[3],
-                                    rw.extra.x, rw.extra.y};
-            uint32_t c[6];
-#pragma unroll
-            for (int i = 0; i < 5; ++i) c[i] = __builtin_amdgcn_alignbit(w6[i + 1], w6[i], W.qshift);
-            c[5] = w6[5] >> W.qshift;
-            ccq432_decode64(c, fin24, mzp24, p);
-          } else {
-            const uint32_t c[5] = {rw.codes[0], rw.codes[1], rw.codes[2], rw.codes[3], rw.extra.x};
-            ccqh_decode64(c, fin24, mzp24, p);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 B0 = {p[8 * q], p[8 * q + 1], p[8 * q + 2], p[8 * q + 3]};
-            const u32x4 B1 = {p[8 * q + 4], p[8 * q + 5], p[8 * q + 6], p[8 * q + 7]};
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              const u32x4 A0 = *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32);
-              const u32x4 A1 =
-                  *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32 + 16);
-              acc[t] = mfma16x16x32(A0, B0, acc[t]);
-              acc[t] = mfma16x16x32(A1, B1, acc[t]);
-            }
-          }
-          continue;
-        }
-        // s24 = s * 2^24 (the decode helpers' scaled form), mzs = -z * s
-        float s24 = 0.0f, mzs = 0.0f;
-        if constexpr (FMT == FMT_CCQ2) {
-          s24 = (float)((rw.scale >> W.qshift) & 0xFu) * fin24;  // = fl(s_q * super) * 2^24
-          mzs = s24 * mzp24;
-        } else if constexpr (FMT == FMT_INT4) {
-          s24 = bf16_bits_to_f32(rw.scale & 0xFFFFu) * kTwo24;
-          mzs = s24 * (-8.0f / kTwo24);
-        } else if constexpr (FMT == FMT_INT4PC) {
-          s24 = fin24;
-          mzs = fin24 * (-8.0f / kTwo24);
-        } else if constexpr (FMT == FMT_INT8) {
-          s24 = bf16_bits_to_f32(rw.scale & 0xFFFFu) * kTwo24;
-          mzs = s24 * (-128.0f / kTwo24);
-        } else if constexpr (FMT == FMT_INT8PC) {
-          s24 = fin24;
-          mzs = fin24 * (-128.0f / kTwo24);
-        } else {
-          const float s = bf16_bits_to_f32(rw.scale & 0xFFFFu);
-          s24 = s * kTwo24;
-          mzs = -(float)(rw.zero & 0xFFu) * s;
-        }
-        // 16 weights (two MFMAs) at a time
-#pragma unroll
-        for (int q = 0; q < WPL / 16; ++q) {
-          uint32_t p[8];
-          if constexpr (FMT == FMT_CCQ2) {
-            ccq_decode16<CLAMP>(rw.codes[q], cs24, W.cz, s24, mzs, p);
-          } else if constexpr (is_int4(FMT)) {
-            int4_decode16(rw.codes[2 * q], rw.codes[2 * q + 1], s24, mzs, p);
-          } else if constexpr (is_int8(FMT)) {
-            int8_decode16(rw.codes, s24, mzs, p);
-          } else {
-            affine2_decode16(rw.codes[q], s24, mzs, p);
-          }
-          const u32x4 B0 = {p[0], p[1], p[2], p[3]};
-          const u32x4 B1 = {p[4], p[5], p[6], p[7]};
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            const u32x4 A0 = *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32);
-            const u32x4 A1 = *reinterpret_cast<const u32x4*>(abase + t * 16 * PITCH + q * 32 + 16);
-            acc[t] = mfma16x16x32(A0, B0, acc[t]);
-            acc[t] = mfma16x16x32(A1, B1, acc[t]);
-          }
-        }
+        step_mma<FMT, MT, CLAMP>(r[j], W, cs24, fin24, mzp24,
+                                 &lds[buf][nl * PITCH + (kw * KCW + j * SSK + kb * WPL) * 2],
+                                 16 * PITCH, acc);
       }
     };
 
@@ -464,6 +475,151 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
     run(std::integral_constant<bool, true>{});
 }
 
+// ---------------------------------------------------------------------------------------------
+// Dense products with at most 16 activation rows whose activation block fits in LDS whole.
+// The chunked kernel above pays a memory round trip per chunk (staging loads, LDS store,
+// barrier); at these sizes that chain, not bandwidth or decode, sets the call time.  Here the
+// activations are staged once and a wave issues the weight loads of up to GNSB steps before its
+// first decode, so a call costs about one round trip plus the decode.  One workgroup per 16
+// output channels; its KS waves (4, or 16 when there are few output tiles) split K into parts of Kpp = K / KS columns, summed in LDS in order.  LDS: the
+// activation rows (pitch 2 K + 16 bytes), then a 128-byte zero block that the lanes of a step
+// running past their part read instead; lanes of padding rows (nl >= M) read row 0 and their
+// results are never stored.
+// ---------------------------------------------------------------------------------------------
+constexpr int GEMV_LDS_MAX = 135168;  // 132 KiB: 16 rows of K = 4096 (one workgroup per CU)
+
+// Steps whose packed data a lane holds at once (2048 columns of a wave's part with 4 waves, 1024
+// with 16: their parts are shorter and their register budget smaller).
+template <int FMT, int KS>
+__host__ __device__ constexpr int gemv_steps() {
+  return (KS == 4 ? 2 : 1) * (is_int8(FMT) ? 8 : is_int4(FMT) ? 8 : 4);
+}
+
+template <int FMT, int KS>
+__global__ __launch_bounds__(64 * KS) void gemv_kernel(const SkinnyArgs args) {
+  constexpr int WPL = lane_weights<FMT>();
+  constexpr int SSK = 4 * WPL;
+  constexpr int GNSB = gemv_steps<FMT, KS>();
+  constexpr int NT = 64 * KS;               // threads
+  constexpr int XB = KS == 4 ? 16 : 8;      // 16-byte activation blocks per thread per round
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int kw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15;
+  const int kb = lane >> 4;
+  const int64_t N = args.N;
+  const int32_t M = (int32_t)args.M;                // 1 .. 16 (checked on the host)
+  const int32_t Kpp = (int32_t)(args.K / KS);        // a multiple of 64 (checked on the host)
+  const int32_t ns = (Kpp + SSK - 1) / SSK;          // steps per wave
+  const int32_t pitch = (int32_t)(args.K * 2 + 16);  // bytes per LDS activation row
+  const int32_t bpr = (int32_t)(args.K / 8);         // 16-byte blocks per activation row
+
+  const int64_t nrow = (int64_t)blockIdx.x * 16 + nl;
+  const bool nvalid = nrow < N;
+  const WaveW<FMT> W = wave_weight<FMT>(args.w0, 0, nvalid ? nrow : (N - 1), kb, (kw * Kpp) >> 6);
+  const float cs24 = W.cs * kTwo24, fin24 = W.fin * kTwo24;
+  const float mzp24 = -(float)args.w0.zp / kTwo24;
+
+  // Weight loads of the first GNSB steps (steps past the part are not loaded), then the
+  // activation block: every load is in flight before the first wait.
+  Raw<FMT> raw[GNSB];
+#pragma unroll
+  for (int j = 0; j < GNSB; ++j)
+    if (j < ns) load_raw<FMT>(raw[j], W, j);
+  // Staged in rounds of XB blocks per thread (one round up to 64 or 128 KiB).  Block b = row r,
+  // column block c.  r = trunc((b + 1/2) * fl(1 / bpr)) in fp32 is floor(b / bpr): the exact
+  // quotient lies at least 1 / (2 bpr) from an integer, and the fp32 error, a few ulp of a value
+  // below 2^9 (b < 16384, bpr >= 32), stays far below that margin.
+  const float inv = 1.0f / (float)bpr;
+  const int32_t nblk = M * bpr;
+  for (int32_t base = 0; base < nblk; base += XB * NT) {
+    auto split = [&](int i, int32_t& r, int32_t& c) {
+      const int32_t b = base + tid + NT * i;
+      r = (int32_t)(((float)b + 0.5f) * inv);
+      c = b - r * bpr;
+    };
+    u32x4 xr[XB];
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      int32_t r, c;
+      split(i, r, c);
+      if (r < M)
+        xr[i] = *reinterpret_cast<const u32x4*>(args.a + (int64_t)r * args.a_stride + (int64_t)c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      int32_t r, c;
+      split(i, r, c);
+      if (r < M) *reinterpret_cast<u32x4*>(lds_raw + r * pitch + c * 16) = xr[i];
+    }
+  }
+  uint8_t* zero_blk = lds_raw + M * pitch;
+  if (tid < 8) reinterpret_cast<u32x4*>(zero_blk)[tid] = (u32x4){0, 0, 0, 0};
+  __syncthreads();
+
+  const uint8_t* arow = lds_raw + (nl < M ? nl : 0) * pitch + (kw * Kpp + kb * WPL) * 2;
+  f32x4 acc[1] = {(f32x4){0.f, 0.f, 0.f, 0.f}};
+  auto run = [&](auto clamp_tag) {
+    constexpr bool CLAMP = decltype(clamp_tag)::value;
+    for (int32_t s0 = 0; s0 < ns; s0 += GNSB) {
+      if (s0 > 0) {
+#pragma unroll
+        for (int j = 0; j < GNSB; ++j)
+          if (s0 + j < ns) load_raw<FMT>(raw[j], W, s0 + j);
+      }
+#pragma unroll
+      for (int j = 0; j < GNSB; ++j) {
+        const int32_t st = s0 + j;
+        if (st >= ns) break;
+        // this lane's first column of the step inside its part; past the part it reads zeros
+        const bool inside = st * SSK + kb * WPL < Kpp;
+        step_mma<FMT, 1, CLAMP>(raw[j], W, cs24, fin24, mzp24,
+                                inside ? arow + st * SSK * 2 : zero_blk, 0, acc);
+      }
+    }
+  };
+  bool no_clamp = false;
+  if constexpr (FMT == FMT_CCQ2) no_clamp = __all(ccq_row_needs_no_clamp(W.cs, W.cz));
+  if (no_clamp)
+    run(std::integral_constant<bool, false>{});
+  else
+    run(std::integral_constant<bool, true>{});
+
+  // K parts summed in order by wave 0, which writes the rows 4 kb + i of its column.
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds_raw);
+  if (kw > 0) red[(kw - 1) * 64 + lane] = acc[0];
+  __syncthreads();
+  if (kw == 0 && nvalid) {
+#pragma unroll
+    for (int p = 1; p < KS; ++p) acc[0] += red[(p - 1) * 64 + lane];
+    uint16_t* y = reinterpret_cast<uint16_t*>(args.out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * kb + i;
+      if (m < M) y[(int64_t)m * args.out_stride + nrow] = (uint16_t)f32_to_bf16_bits(acc[0][i]);
+    }
+  }
+}
+
+template <int FMT, int KS>
+hipError_t launch_gemv_ks(const SkinnyArgs& a, size_t lds_bytes, hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};  // per instantiation, one bit per device
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, KS>),
+                                    GEMV_LDS_MAX, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemv_kernel<FMT, KS>), dim3((unsigned)((a.N + 15) / 16)), dim3(64 * KS),
+                     lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_gemv_fmt(const SkinnyArgs& a, int ks, size_t lds_bytes, hipStream_t s) {
+  return ks == 16 ? launch_gemv_ks<FMT, 16>(a, lds_bytes, s) : launch_gemv_ks<FMT, 4>(a, lds_bytes, s);
+}
+
 template <int FMT, int MT, int MODE, int KSPLIT>
 hipError_t launch_one(const SkinnyArgs& a, int64_t gy, int64_t gz, hipStream_t s) {
   constexpr int KCT = chunk_cols<FMT, KSPLIT>() * KSPLIT;
@@ -516,6 +672,33 @@ hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const Skinn
     case FMT_CCQH:
       return launch_fmt<FMT_CCQH>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
     default: return launch_fmt<FMT_CCQ2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+  }
+}
+
+bool gemv_fits(int64_t m, int64_t n, int64_t k) {
+  return m >= 1 && m <= 16 && k % 256 == 0 && k < (1ll << 30) && (n + 15) / 16 <= 0x7FFFFFFF &&
+         m * (2 * k + 16) + 128 <= GEMV_LDS_MAX;
+}
+
+hipError_t launch_gemv(int fmt, const SkinnyArgs& args, hipStream_t stream) {
+  if (!gemv_fits(args.M, args.N, args.K)) return hipErrorInvalidValue;
+  // 16 waves per output tile when 4 would leave at least half of the 1024 SIMDs idle (each
+  // part a multiple of 64 columns); with 8 the compiler runs out of registers
+  const int64_t ntiles = (args.N + 15) / 16;
+  const int ks = (ntiles * 16 <= 2048 && args.K % 1024 == 0) ? 16 : 4;
+  int64_t lds = args.M * (2 * args.K + 16) + 128;
+  if (lds < (ks - 1) * 1024) lds = (ks - 1) * 1024;  // the K-part sums reuse it
+  switch (fmt) {
+    case FMT_INT4:
+      if (args.w0.group == 0) return launch_gemv_fmt<FMT_INT4PC>(args, ks, lds, stream);
+      return launch_gemv_fmt<FMT_INT4>(args, ks, lds, stream);
+    case FMT_AFFINE2: return launch_gemv_fmt<FMT_AFFINE2>(args, ks, lds, stream);
+    case FMT_INT8:
+      if (args.w0.group == 0) return launch_gemv_fmt<FMT_INT8PC>(args, ks, lds, stream);
+      return launch_gemv_fmt<FMT_INT8>(args, ks, lds, stream);
+    case FMT_CCQ432: return launch_gemv_fmt<FMT_CCQ432>(args, ks, lds, stream);
+    case FMT_CCQH: return launch_gemv_fmt<FMT_CCQH>(args, ks, lds, stream);
+    default: return launch_gemv_fmt<FMT_CCQ2>(args, ks, lds, stream);
   }
 }
 
