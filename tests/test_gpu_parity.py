@@ -302,7 +302,8 @@ def test_gemm_alg2_random_words_bit_exact(wq, name):
                                                  (300, 8, 64, "uniform"), (4096, 8, 64, "zipf"),
                                                  (33, 4, 300, "uniform"), (50, 1, 1, "uniform"),
                                                  (20, 8, 512, "uniform"), (1000, 6, 16, "zipf"),
-                                                 (0, 8, 64, "uniform")])
+                                                 (0, 8, 64, "uniform"), (128, 8, 64, "zipf"),
+                                                 (129, 8, 64, "zipf")])
 def test_route_exact(wq, t, topk, experts, kind):
     import torch
 
@@ -313,6 +314,27 @@ def test_route_exact(wq, t, topk, experts, kind):
     off, pairs = wq.wq_moe_route(torch.from_numpy(ids).cuda(), experts)
     assert np.array_equal(off.cpu().numpy(), off_ref)
     assert np.array_equal(pairs.cpu().numpy(), pairs_ref)
+
+
+@pytest.mark.parametrize("t,experts", [(40, 64), (300, 16)])
+def test_route_drops_ids_out_of_range(wq, t, experts):
+    # Ids outside [0, E) are dropped: the offsets count the valid pairs only and the first
+    # offsets[E] slots hold the valid pairs grouped by expert in increasing pair order (checked
+    # against a direct count, since the oracle refuses such tables).  40 x 8 pairs take the
+    # few-pairs kernel, 300 x 8 the counter-row kernel.
+    import torch
+
+    ids, _ = synth.routing_uniform(t, 8, experts, 9, t)
+    flat = ids.reshape(-1).copy()
+    bad = np.random.default_rng(10).random(flat.size) < 0.1
+    flat[bad] = np.where(np.arange(flat.size)[bad] % 2 == 0, -1, experts)
+    ids = flat.reshape(ids.shape)
+    off, pairs = wq.wq_moe_route(torch.from_numpy(ids).cuda(), experts)
+    off, pairs = off.cpu().numpy(), pairs.cpu().numpy()
+    counts = np.array([(flat == e).sum() for e in range(experts)])
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(counts)]))
+    want = np.concatenate([np.flatnonzero(flat == e) for e in range(experts)])
+    assert np.array_equal(pairs[:off[-1]], want)
 
 
 MOE_CASES = [

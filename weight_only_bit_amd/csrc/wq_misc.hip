@@ -207,6 +207,82 @@ __global__ __launch_bounds__(ROUTE_MAX_THREADS) void route_kernel(const int32_t*
 }
 
 // ---------------------------------------------------------------------------------------------
+// Routing of few pairs (at most ROUTE_SMALL_PAIRS, a decode step): the counter rows above cost
+// more than the pairs themselves.  One thread per pair; wave c holds the pairs 64 c .. 64 c + 63.
+// Each lane finds the lanes of its wave with the same expert from ten ballots over the bits of
+// its id (E <= 512; dropped pairs carry the id E, which no expert matches), so its rank among
+// them is a population count of the lower lanes.  The first lane of each such group writes the
+// group's size to the wave's row of an LDS histogram; per expert, the rows' exclusive prefix over
+// waves plus the expert's offset is the slot of the wave's first pair of that expert.  Equal ids
+// therefore keep increasing p -- the stable order of the kernel above.
+// ---------------------------------------------------------------------------------------------
+constexpr int ROUTE_SMALL_PAIRS = 1024;
+constexpr int ROUTE_MAX_EXPERTS = ROUTE_LDS_COUNTERS / 64;  // 512
+
+__global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __restrict__ ids,
+                                                           int32_t npairs, int32_t experts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted) {
+  __shared__ int32_t s_hist[ROUTE_SMALL_PAIRS / 64 * ROUTE_MAX_EXPERTS];  // [wave][expert]
+  __shared__ int32_t s_base[ROUTE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const int T = blockDim.x;  // 64 * ceil(npairs / 64), at least 64
+  const int lane = tid & 63;
+  const int c = tid >> 6;
+  const int nc = T >> 6;
+  const int E = experts;
+  int e = E;
+  if (tid < npairs) {
+    const int v = ids[tid];
+    if (v >= 0 && v < E) e = v;
+  }
+  for (int i = tid; i < nc * ROUTE_MAX_EXPERTS; i += T) s_hist[i] = 0;
+  uint64_t same = ~0ull;  // lanes of this wave with the same id
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  const int within = __popcll(same & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (e < E && within == 0) s_hist[c * ROUTE_MAX_EXPERTS + e] = __popcll(same);
+  __syncthreads();
+  for (int x = tid; x < E; x += T) {  // per expert: prefix over waves, total
+    int32_t run = 0;
+    for (int w = 0; w < nc; ++w) {
+      const int32_t v = s_hist[w * ROUTE_MAX_EXPERTS + x];
+      s_hist[w * ROUTE_MAX_EXPERTS + x] = run;
+      run += v;
+    }
+    s_base[x] = run;
+  }
+  __syncthreads();
+  // exclusive scan of the totals (wave 0; lane l takes a block of experts)
+  if (tid < 64) {
+    const int per = (E + 63) / 64;
+    const int e0 = tid * per;
+    int32_t local = 0;
+    for (int x = e0; x < e0 + per && x < E; ++x) local += s_base[x];
+    int32_t incl = local;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t v = __shfl_up(incl, d);
+      if (tid >= d) incl += v;
+    }
+    int32_t run = incl - local;
+    for (int x = e0; x < e0 + per && x < E; ++x) {
+      const int32_t tot = s_base[x];
+      s_base[x] = run;
+      offsets[x] = run;
+      run += tot;
+    }
+    if (tid == 63) offsets[E] = incl;
+  }
+  __syncthreads();
+  if (e < E) sorted[s_base[e] + s_hist[c * ROUTE_MAX_EXPERTS + e] + within] = tid;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Combine: y[t][c] = bf16( sum_j w[t][j] * d[t*topk + j][c] ), slots summed in order j with
 // fp32 fused multiply-adds.  One thread per 4 columns.
 // ---------------------------------------------------------------------------------------------
@@ -257,6 +333,12 @@ hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t
 hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int32_t* offsets,
                         int32_t* sorted_pairs, hipStream_t stream) {
   if (experts <= 0 || experts > ROUTE_LDS_COUNTERS / 64) return hipErrorInvalidValue;
+  if (npairs <= ROUTE_SMALL_PAIRS) {
+    const int64_t t = npairs < 64 ? 64 : (npairs + 63) / 64 * 64;
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3((unsigned)t), 0, stream, ids,
+                       (int32_t)npairs, experts, offsets, sorted_pairs);
+    return hipGetLastError();
+  }
   const int T = route_threads(experts);
   const int S = T >= experts ? T / experts : 1;
   const size_t lds = sizeof(int32_t) * ((size_t)T * experts + (size_t)S * experts + experts);
