@@ -356,6 +356,16 @@ int moe_row_tiles(int64_t t, int32_t topk, int64_t experts) {
   return ((double)t * topk / (double)experts <= 8.0) ? 1 : 2;
 }
 
+// Activation columns per LDS chunk of the decode-streaming MoE kernels: 2048 when the routed
+// work makes at most 256 workgroups (one per CU at that chunk size; each chunk costs a memory
+// round trip, so fewer, longer chunks shorten a call that few workgroups run), else 512.
+int moe_chunk(const wq_weight* w, int64_t t, int32_t topk, int tiles_per_wg) {
+  if (moe_row_tiles(t, topk, w->experts) != 1) return 512;
+  const int64_t active = t * topk < w->experts ? t * topk : w->experts;
+  const int64_t wgs = active * (((w->n + 15) / 16 + tiles_per_wg - 1) / tiles_per_wg);
+  return wgs <= 256 ? 2048 : 512;
+}
+
 bool moe_tiled(const wq_weight* w, int64_t t, int32_t topk) {
   return has_tiled(w) && (double)t * topk / (double)w->experts >= kMoeTiledRows;
 }
@@ -403,7 +413,7 @@ hipError_t run_gate_up(const uint16_t* x, int64_t t, const int32_t* offsets, con
   a.N = gate->n;
   a.K = gate->k;
   return wq::launch_skinny(gate->format, wq::MODE_GATEUP, moe_row_tiles(t, topk, gate->experts), 1,
-                           a, gate->experts, 1, s);
+                           a, gate->experts, 1, s, moe_chunk(gate, t, topk, 2));
 }
 
 hipError_t run_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* offsets,
@@ -433,7 +443,7 @@ hipError_t run_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* o
   a.N = down->n;
   a.K = down->k;
   return wq::launch_skinny(down->format, wq::MODE_DOWN, moe_row_tiles(t, topk, down->experts), 1,
-                           a, down->experts, 1, s);
+                           a, down->experts, 1, s, moe_chunk(down, t, topk, 4));
 }
 
 }  // namespace

@@ -43,9 +43,10 @@ enum { MODE_DENSE = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
 
 // Launch the skinny kernel for format `fmt`; m_tiles = 1 or 2 (16 or 32 activation rows per
 // pass); ksplit = 1 or 4 (waves of a workgroup split K); grid_y = experts (MoE) or 1;
-// grid_z = row super-tiles (dense).
+// grid_z = row super-tiles (dense); chunk = activation columns per LDS chunk, 512 or (MoE
+// modes with m_tiles = 1 only) 2048.
 hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
-                         int64_t grid_y, int64_t grid_z, hipStream_t stream);
+                         int64_t grid_y, int64_t grid_z, hipStream_t stream, int chunk = 512);
 
 // Dense products of 1..16 activation rows whose rows fit in LDS whole (rows x (2 K + 16) bytes
 // plus 128 at most 132 KiB) with K % 256 == 0: one launch, the waves of a workgroup split K.

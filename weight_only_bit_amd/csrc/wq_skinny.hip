@@ -43,9 +43,9 @@ template <int FMT>
 __host__ __device__ constexpr int lane_weights() { return is_int8(FMT) ? 16 : is_int4(FMT) ? 32 : 64; }
 
 // Columns per wave per LDS chunk: at least one step (4 lanes x lane_weights).
-template <int FMT, int KSPLIT>
+template <int FMT, int KSPLIT, int KCB = KCT_BASE>
 __host__ __device__ constexpr int chunk_cols() {
-  return (KCT_BASE / KSPLIT) > 4 * lane_weights<FMT>() ? KCT_BASE / KSPLIT : 4 * lane_weights<FMT>();
+  return (KCB / KSPLIT) > 4 * lane_weights<FMT>() ? KCB / KSPLIT : 4 * lane_weights<FMT>();
 }
 
 // Packed data of one step for one lane: 16 bytes of its row and its group's scale.
@@ -252,11 +252,14 @@ __device__ __forceinline__ void step_mma(const Raw<FMT>& rw, const WaveW<FMT>& W
   }
 }
 
-template <int FMT, int MT, int MODE, int KSPLIT>
+// KCB: activation columns per LDS chunk -- 512 (four workgroups per CU), or 2048 for launches
+// with few workgroups (one per CU), where each chunk's memory round trip, not the decode, sets
+// the time.
+template <int FMT, int MT, int MODE, int KSPLIT, int KCB = KCT_BASE>
 __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   constexpr int WPL = lane_weights<FMT>();     // weights per lane per step
   constexpr int SSK = 4 * WPL;                 // k per step
-  constexpr int KCW = chunk_cols<FMT, KSPLIT>();  // columns per wave per chunk
+  constexpr int KCW = chunk_cols<FMT, KSPLIT, KCB>();  // columns per wave per chunk
   constexpr int KCT = KCW * KSPLIT;
   constexpr int SPC = KCW / SSK;               // steps per wave per chunk
   constexpr int ROWS = MT * 16;
@@ -620,24 +623,28 @@ hipError_t launch_gemv_fmt(const SkinnyArgs& a, int ks, size_t lds_bytes, hipStr
   return ks == 16 ? launch_gemv_ks<FMT, 16>(a, lds_bytes, s) : launch_gemv_ks<FMT, 4>(a, lds_bytes, s);
 }
 
-template <int FMT, int MT, int MODE, int KSPLIT>
+template <int FMT, int MT, int MODE, int KSPLIT, int KCB = KCT_BASE>
 hipError_t launch_one(const SkinnyArgs& a, int64_t gy, int64_t gz, hipStream_t s) {
-  constexpr int KCT = chunk_cols<FMT, KSPLIT>() * KSPLIT;
+  constexpr int KCT = chunk_cols<FMT, KSPLIT, KCB>() * KSPLIT;
   constexpr size_t lds_bytes = 2 * (size_t)(MT * 16) * (KCT * 2 + 16);
   constexpr int TPW = (KSPLIT == 4) ? 1 : (MODE == MODE_GATEUP ? 2 : 4);
   static std::atomic<uint64_t> lds_set{0};  // per instantiation, one bit per device
   hipError_t e = ensure_dynamic_lds(
-      reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, MODE, KSPLIT>), (int)lds_bytes, lds_set);
+      reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, MODE, KSPLIT, KCB>), (int)lds_bytes, lds_set);
   if (e != hipSuccess) return e;
   const int64_t ntiles = (a.N + 15) / 16;
   dim3 grid((unsigned)((ntiles + TPW - 1) / TPW), (unsigned)gy, (unsigned)gz);
-  hipLaunchKernelGGL((skinny_kernel<FMT, MT, MODE, KSPLIT>), grid, dim3(256), lds_bytes, s, a);
+  hipLaunchKernelGGL((skinny_kernel<FMT, MT, MODE, KSPLIT, KCB>), grid, dim3(256), lds_bytes, s, a);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_fmt(int mode, int mt, int ksplit, const SkinnyArgs& a, int64_t gy, int64_t gz,
-                      hipStream_t s) {
+                      hipStream_t s, int chunk) {
+  if (chunk == 2048 && mt == 1 && mode == MODE_GATEUP)
+    return launch_one<FMT, 1, MODE_GATEUP, 1, 2048>(a, gy, gz, s);
+  if (chunk == 2048 && mt == 1 && mode == MODE_DOWN)
+    return launch_one<FMT, 1, MODE_DOWN, 1, 2048>(a, gy, gz, s);
   if (mode == MODE_DENSE) {
     if (ksplit == 4)
       return mt == 1 ? launch_one<FMT, 1, MODE_DENSE, 4>(a, gy, gz, s)
@@ -655,23 +662,23 @@ hipError_t launch_fmt(int mode, int mt, int ksplit, const SkinnyArgs& a, int64_t
 }  // namespace
 
 hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
-                         int64_t grid_y, int64_t grid_z, hipStream_t stream) {
+                         int64_t grid_y, int64_t grid_z, hipStream_t stream, int chunk) {
   switch (fmt) {
     case FMT_INT4:
       if (args.w0.group == 0)
-        return launch_fmt<FMT_INT4PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
-      return launch_fmt<FMT_INT4>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+        return launch_fmt<FMT_INT4PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
+      return launch_fmt<FMT_INT4>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
     case FMT_AFFINE2:
-      return launch_fmt<FMT_AFFINE2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+      return launch_fmt<FMT_AFFINE2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
     case FMT_INT8:
       if (args.w0.group == 0)
-        return launch_fmt<FMT_INT8PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
-      return launch_fmt<FMT_INT8>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+        return launch_fmt<FMT_INT8PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
+      return launch_fmt<FMT_INT8>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
     case FMT_CCQ432:
-      return launch_fmt<FMT_CCQ432>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+      return launch_fmt<FMT_CCQ432>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
     case FMT_CCQH:
-      return launch_fmt<FMT_CCQH>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
-    default: return launch_fmt<FMT_CCQ2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+      return launch_fmt<FMT_CCQH>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
+    default: return launch_fmt<FMT_CCQ2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
   }
 }
 
