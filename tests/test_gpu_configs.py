@@ -126,3 +126,23 @@ def test_moe_prefill_layer_full_size(wq):
     t_light = int(np.nonzero((ids == light).any(axis=1))[0][-1])
     tokens = np.array(sorted({t_heavy, t_light, T - 1}), np.int32)
     _check_tokens(wq, mats, x, ids, wts, tokens, "moe prefill full size ccq")
+
+
+@pytest.mark.parametrize("name,tokens", [("ccq", 1), ("ccq", 4), ("int4", 1)])
+def test_moe_pages_grouped_shape(wq, name, tokens):
+    # The pages' grouped-GEMM shape: 256 experts, hidden 7168, expert intermediate 512, top-8,
+    # one or four tokens (the single-staging kernels); every token against the oracle.
+    fmt, group = {"ccq": (oracle.CCQ, 64), "int4": (oracle.INT4, 64)}[name]
+    n_exp, hidden, inter = 256, 7168, 512
+    _say(f"pages grouped shape {name} tokens={tokens}: drawing weights")
+    mats = []
+    for j, (n, k) in enumerate(((inter, hidden), (inter, hidden), (hidden, inter))):
+        arr = synth.random_packed_device(fmt, n_exp, n, k, 840 + j, group=group)
+        mats.append(wq.PackedWeight(fmt, n, k, n_exp, group,
+                                    *(arr.get(f) for f in ("codes", "scales", "zeros", "qscale",
+                                                            "super_scale", "code_scale",
+                                                            "code_zero")),
+                                    oracle.default_zp(fmt)))
+    x = synth.acts_bf16((tokens, hidden), 843, tokens)
+    ids, wts = synth.routing_uniform(tokens, 8, n_exp, 844, tokens)
+    _check_tokens(wq, mats, x, ids, wts, np.arange(tokens), f"pages grouped {name} t={tokens}")

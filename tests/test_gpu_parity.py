@@ -375,6 +375,44 @@ def test_moe_ffn_parity(wq, case):
     assert_close(torch_bf16_bits(y), ref, f"moe {case}")
 
 
+# MoE products of at most 16 tokens whose (expert, 16-row tile) pairs number at most 256 take the
+# single-staging kernel: 16 waves per workgroup when K splits, else 4 ((4,3,2) and hybrid: always
+# 4); an expert with more rows than fit in LDS at once takes several passes.  The other products
+# of these cases take the chunked kernel.
+MOE_GEMV_CASES = [
+    # name, E, hidden, inter, tokens, topk, routing
+    ("ccq", 8, 1024, 512, 1, 2, "uniform"),      # gate+up 16 waves, down 4
+    ("int4", 8, 768, 256, 3, 2, "uniform"),      # gate+up 4 waves, ragged parts
+    ("int8pc", 4, 8192, 256, 16, 2, "expert0"),  # gate+up: expert 0 has 16 rows, two passes of 8
+    ("ccq432", 8, 512, 256, 4, 2, "uniform"),    # both products, 4 waves
+    ("affine2", 8, 768, 512, 2, 2, "uniform"),   # both products, 4 waves
+    ("ccq", 8, 2048, 1024, 1, 1, "uniform"),     # down 16 waves
+    ("int4pc", 8, 1024, 512, 5, 3, "uniform"),   # gate+up 16 waves at 256 pairs
+    ("ccqh", 6, 1024, 256, 2, 2, "uniform"),     # both products, 4 waves
+]
+
+
+@pytest.mark.parametrize("case", MOE_GEMV_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_moe_gemv_path_parity(wq, case):
+    import torch
+
+    name, E, H, I, T, topk, kind = case
+    fmt, group = _fmt_group(name)
+    _say(f"moe gemv {case}")
+    gate = _quant(fmt, (E, I, H), (13, 1, E, H, I), group=group)
+    up = _quant(fmt, (E, I, H), (13, 2, E, H, I), group=group)
+    down = _quant(fmt, (E, H, I), (13, 3, E, H, I), group=group)
+    x = synth.acts_bf16((T, H), 14, T, H)
+    ids, wts = synth.routing_uniform(T, topk, E, 15, T)
+    if kind == "expert0":  # every token's first expert is 0, the others distinct from it
+        for t in range(T):
+            ids[t] = [0] + [1 + (t + j) % (E - 1) for j in range(topk - 1)]
+    ref = oracle.moe_ffn(x, ids, wts, gate, up, down)
+    y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(wts).cuda(), to_device(gate), to_device(up), to_device(down))
+    assert_close(torch_bf16_bits(y), ref, f"moe gemv {case}")
+
+
 def test_empty_inputs(wq):
     # no rows, no tokens: nothing to compute, no error, empty outputs
     import torch

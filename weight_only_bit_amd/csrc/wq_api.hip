@@ -356,14 +356,13 @@ int moe_row_tiles(int64_t t, int32_t topk, int64_t experts) {
   return ((double)t * topk / (double)experts <= 8.0) ? 1 : 2;
 }
 
-// Activation columns per LDS chunk of the decode-streaming MoE kernels: 2048 when the routed
-// work makes at most 256 workgroups (one per CU at that chunk size; each chunk costs a memory
-// round trip, so fewer, longer chunks shorten a call that few workgroups run), else 512.
-int moe_chunk(const wq_weight* w, int64_t t, int32_t topk, int tiles_per_wg) {
-  if (moe_row_tiles(t, topk, w->experts) != 1) return 512;
+// The single-staging kernel for MoE products of at most 16 tokens (so an expert's rows, one per
+// token routed to it, take one pass of up to 16 rows when they fit) with few workgroups: the
+// waves per workgroup, or 0 for the chunked kernel.
+int moe_gemv_split(int mode, const wq_weight* w, int64_t t, int32_t topk) {
+  if (t > 16) return 0;
   const int64_t active = t * topk < w->experts ? t * topk : w->experts;
-  const int64_t wgs = active * (((w->n + 15) / 16 + tiles_per_wg - 1) / tiles_per_wg);
-  return wgs <= 256 ? 2048 : 512;
+  return wq::gemv_moe_split(w->format, mode, active, w->n, w->k);
 }
 
 bool moe_tiled(const wq_weight* w, int64_t t, int32_t topk) {
@@ -412,8 +411,10 @@ hipError_t run_gate_up(const uint16_t* x, int64_t t, const int32_t* offsets, con
   a.out_stride = gate->n;
   a.N = gate->n;
   a.K = gate->k;
+  if (const int ks = moe_gemv_split(wq::MODE_GATEUP, gate, t, topk))
+    return wq::launch_gemv_moe(gate->format, wq::MODE_GATEUP, a, gate->experts, ks, s);
   return wq::launch_skinny(gate->format, wq::MODE_GATEUP, moe_row_tiles(t, topk, gate->experts), 1,
-                           a, gate->experts, 1, s, moe_chunk(gate, t, topk, 2));
+                           a, gate->experts, 1, s);
 }
 
 hipError_t run_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* offsets,
@@ -442,8 +443,10 @@ hipError_t run_down(const uint16_t* h, int64_t t, int32_t topk, const int32_t* o
   a.out_stride = down->n;
   a.N = down->n;
   a.K = down->k;
+  if (const int ks = moe_gemv_split(wq::MODE_DOWN, down, t, topk))
+    return wq::launch_gemv_moe(down->format, wq::MODE_DOWN, a, down->experts, ks, s);
   return wq::launch_skinny(down->format, wq::MODE_DOWN, moe_row_tiles(t, topk, down->experts), 1,
-                           a, down->experts, 1, s, moe_chunk(down, t, topk, 4));
+                           a, down->experts, 1, s);
 }
 
 }  // namespace

@@ -43,15 +43,23 @@ enum { MODE_DENSE = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
 
 // Launch the skinny kernel for format `fmt`; m_tiles = 1 or 2 (16 or 32 activation rows per
 // pass); ksplit = 1 or 4 (waves of a workgroup split K); grid_y = experts (MoE) or 1;
-// grid_z = row super-tiles (dense); chunk = activation columns per LDS chunk, 512 or (MoE
-// modes with m_tiles = 1 only) 2048.
+// grid_z = row super-tiles (dense).
 hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
-                         int64_t grid_y, int64_t grid_z, hipStream_t stream, int chunk = 512);
+                         int64_t grid_y, int64_t grid_z, hipStream_t stream);
 
-// Dense products of 1..16 activation rows whose rows fit in LDS whole (rows x (2 K + 16) bytes
-// plus 128 at most 132 KiB) with K % 256 == 0: one launch, the waves of a workgroup split K.
+// Single-staging products: activation rows staged in LDS whole, rows x (2 K + 16) + 128 bytes
+// at most 132 KiB, K % 256 == 0.  gemv_pass_rows(k): rows of one pass (at most 16, 0 if none).
+int gemv_pass_rows(int64_t k);
+// Dense products of 1 .. gemv_pass_rows(k) rows: one launch, the waves of a workgroup split K.
 bool gemv_fits(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemv(int fmt, const SkinnyArgs& args, hipStream_t stream);
+// MoE gate+up / down over `experts` (grid y), each expert's routed rows in passes of
+// gemv_pass_rows(K).  gemv_moe_split: the waves per workgroup (4 or 16) for a launch whose
+// routed work touches at most `active_experts` experts, or 0 when the chunked kernel is the
+// better choice (many workgroups) or K does not split.
+int gemv_moe_split(int fmt, int mode, int64_t active_experts, int64_t n, int64_t k);
+hipError_t launch_gemv_moe(int fmt, int mode, const SkinnyArgs& args, int64_t experts, int ks,
+                           hipStream_t stream);
 
 hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t* out,
                           hipStream_t stream);

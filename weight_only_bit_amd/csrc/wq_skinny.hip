@@ -43,9 +43,9 @@ template <int FMT>
 __host__ __device__ constexpr int lane_weights() { return is_int8(FMT) ? 16 : is_int4(FMT) ? 32 : 64; }
 
 // Columns per wave per LDS chunk: at least one step (4 lanes x lane_weights).
-template <int FMT, int KSPLIT, int KCB = KCT_BASE>
+template <int FMT, int KSPLIT>
 __host__ __device__ constexpr int chunk_cols() {
-  return (KCB / KSPLIT) > 4 * lane_weights<FMT>() ? KCB / KSPLIT : 4 * lane_weights<FMT>();
+  return (KCT_BASE / KSPLIT) > 4 * lane_weights<FMT>() ? KCT_BASE / KSPLIT : 4 * lane_weights<FMT>();
 }
 
 // Packed data of one step for one lane: 16 bytes of its row and its group's scale.
@@ -252,14 +252,11 @@ __device__ __forceinline__ void step_mma(const Raw<FMT>& rw, const WaveW<FMT>& W
   }
 }
 
-// KCB: activation columns per LDS chunk -- 512 (four workgroups per CU), or 2048 for launches
-// with few workgroups (one per CU), where each chunk's memory round trip, not the decode, sets
-// the time.
-template <int FMT, int MT, int MODE, int KSPLIT, int KCB = KCT_BASE>
+template <int FMT, int MT, int MODE, int KSPLIT>
 __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   constexpr int WPL = lane_weights<FMT>();     // weights per lane per step
   constexpr int SSK = 4 * WPL;                 // k per step
-  constexpr int KCW = chunk_cols<FMT, KSPLIT, KCB>();  // columns per wave per chunk
+  constexpr int KCW = chunk_cols<FMT, KSPLIT>();  // columns per wave per chunk
   constexpr int KCT = KCW * KSPLIT;
   constexpr int SPC = KCW / SSK;               // steps per wave per chunk
   constexpr int ROWS = MT * 16;
@@ -479,107 +476,173 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense products with at most 16 activation rows whose activation block fits in LDS whole.
-// The chunked kernel above pays a memory round trip per chunk (staging loads, LDS store,
-// barrier); at these sizes that chain, not bandwidth or decode, sets the call time.  Here the
-// activations are staged once and a wave issues the weight loads of up to GNSB steps before its
-// first decode, so a call costs about one round trip plus the decode.  One workgroup per 16
-// output channels; its KS waves (4, or 16 when there are few output tiles) split K into parts of Kpp = K / KS columns, summed in LDS in order.  LDS: the
-// activation rows (pitch 2 K + 16 bytes), then a 128-byte zero block that the lanes of a step
-// running past their part read instead; lanes of padding rows (nl >= M) read row 0 and their
-// results are never stored.
+// Single-staging kernel: products of at most 16 activation rows per pass whose rows fit in LDS
+// whole -- a dense product of few rows, or an MoE product of few routed tokens (each expert's
+// rows in passes).  The chunked kernel above pays a memory round trip per chunk (staging loads,
+// LDS store, barrier); at these sizes that chain, not bandwidth or decode, sets the call time.
+// Here the activations are staged once per pass and a wave issues the weight loads of up to GNSB
+// steps before its first decode, so a pass costs about one round trip plus the decode.  One
+// workgroup per 16 output channels (and expert); its KS waves (4, or 16 when there are few
+// output tiles) split K into parts of Kpp columns -- gate+up: half of the waves take the gate
+// matrix and half the up matrix -- summed in LDS in order.  LDS: the pass's activation rows
+// (pitch 2 K + 16 bytes), then a 128-byte zero block that the lanes of a step running past their
+// part read instead; lanes of padding rows (nl >= rows of the pass) read row 0 and their results
+// are never stored.
 // ---------------------------------------------------------------------------------------------
 constexpr int GEMV_LDS_MAX = 135168;  // 132 KiB: 16 rows of K = 4096 (one workgroup per CU)
 
-// Steps whose packed data a lane holds at once (2048 columns of a wave's part with 4 waves, 1024
-// with 16: their parts are shorter and their register budget smaller).
+// Steps whose packed data a lane holds at once (2048 columns of a wave's part with 4 waves, 512
+// with 16: their parts are shorter and their register budget a quarter).
 template <int FMT, int KS>
 __host__ __device__ constexpr int gemv_steps() {
-  return (KS == 4 ? 2 : 1) * (is_int8(FMT) ? 8 : is_int4(FMT) ? 8 : 4);
+  return KS == 4 ? (is_int8(FMT) || is_int4(FMT) ? 16 : 8) : (is_int8(FMT) || is_int4(FMT) ? 4 : 2);
 }
 
-template <int FMT, int KS>
-__global__ __launch_bounds__(64 * KS) void gemv_kernel(const SkinnyArgs args) {
+template <int FMT, int KS, int MODE>
+__global__ __launch_bounds__(64 * KS) void gemv_kernel(const SkinnyArgs args, int32_t pass_rows) {
   constexpr int WPL = lane_weights<FMT>();
   constexpr int SSK = 4 * WPL;
   constexpr int GNSB = gemv_steps<FMT, KS>();
   constexpr int NT = 64 * KS;               // threads
-  constexpr int XB = KS == 4 ? 16 : 8;      // 16-byte activation blocks per thread per round
+  constexpr int XB = KS == 4 ? 16 : 4;      // 16-byte activation blocks per thread per round
+  constexpr int NMAT = MODE == MODE_GATEUP ? 2 : 1;  // gate+up: half of the waves per matrix
+  constexpr int KP = KS / NMAT;                        // K parts per matrix
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+  __shared__ int32_t s_row[16];  // MoE: the pass's token (gate+up) or pair (down) per row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int kw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mat = kw / KP;
+  const int part = kw % KP;
   const int nl = lane & 15;
   const int kb = lane >> 4;
   const int64_t N = args.N;
-  const int32_t M = (int32_t)args.M;                // 1 .. 16 (checked on the host)
-  const int32_t Kpp = (int32_t)(args.K / KS);        // a multiple of 64 (checked on the host)
+  const int32_t Kpp = (int32_t)(args.K / KP);        // a multiple of 64 (checked on the host)
   const int32_t ns = (Kpp + SSK - 1) / SSK;          // steps per wave
   const int32_t pitch = (int32_t)(args.K * 2 + 16);  // bytes per LDS activation row
   const int32_t bpr = (int32_t)(args.K / 8);         // 16-byte blocks per activation row
 
+  int64_t e = 0, m_base = 0, m_total = args.M;  // dense: M <= pass_rows (checked on the host)
+  if constexpr (MODE != MODE_DENSE) {
+    e = blockIdx.y;
+    m_base = args.offsets[e];
+    m_total = args.offsets[e + 1] - m_base;
+    if (m_total <= 0) return;
+  }
+
   const int64_t nrow = (int64_t)blockIdx.x * 16 + nl;
   const bool nvalid = nrow < N;
-  const WaveW<FMT> W = wave_weight<FMT>(args.w0, 0, nvalid ? nrow : (N - 1), kb, (kw * Kpp) >> 6);
+  const WaveW<FMT> W =
+      wave_weight<FMT>(mat ? args.w1 : args.w0, e, nvalid ? nrow : (N - 1), kb, (part * Kpp) >> 6);
   const float cs24 = W.cs * kTwo24, fin24 = W.fin * kTwo24;
   const float mzp24 = -(float)args.w0.zp / kTwo24;
 
-  // Weight loads of the first GNSB steps (steps past the part are not loaded), then the
-  // activation block: every load is in flight before the first wait.
+  // Weight loads of the first GNSB steps (steps past the part are not loaded), issued before the
+  // activation staging so that every load is in flight before the first wait.
   Raw<FMT> raw[GNSB];
 #pragma unroll
   for (int j = 0; j < GNSB; ++j)
     if (j < ns) load_raw<FMT>(raw[j], W, j);
-  // Staged in rounds of XB blocks per thread (one round up to 64 or 128 KiB).  Block b = row r,
-  // column block c.  r = trunc((b + 1/2) * fl(1 / bpr)) in fp32 is floor(b / bpr): the exact
-  // quotient lies at least 1 / (2 bpr) from an integer, and the fp32 error, a few ulp of a value
-  // below 2^9 (b < 16384, bpr >= 32), stays far below that margin.
-  const float inv = 1.0f / (float)bpr;
-  const int32_t nblk = M * bpr;
-  for (int32_t base = 0; base < nblk; base += XB * NT) {
-    auto split = [&](int i, int32_t& r, int32_t& c) {
-      const int32_t b = base + tid + NT * i;
-      r = (int32_t)(((float)b + 0.5f) * inv);
-      c = b - r * bpr;
-    };
-    u32x4 xr[XB];
-#pragma unroll
-    for (int i = 0; i < XB; ++i) {
-      int32_t r, c;
-      split(i, r, c);
-      if (r < M)
-        xr[i] = *reinterpret_cast<const u32x4*>(args.a + (int64_t)r * args.a_stride + (int64_t)c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < XB; ++i) {
-      int32_t r, c;
-      split(i, r, c);
-      if (r < M) *reinterpret_cast<u32x4*>(lds_raw + r * pitch + c * 16) = xr[i];
-    }
-  }
-  uint8_t* zero_blk = lds_raw + M * pitch;
-  if (tid < 8) reinterpret_cast<u32x4*>(zero_blk)[tid] = (u32x4){0, 0, 0, 0};
-  __syncthreads();
 
-  const uint8_t* arow = lds_raw + (nl < M ? nl : 0) * pitch + (kw * Kpp + kb * WPL) * 2;
-  f32x4 acc[1] = {(f32x4){0.f, 0.f, 0.f, 0.f}};
+  const float inv = 1.0f / (float)bpr;
+  uint8_t* zero_blk = lds_raw + pass_rows * pitch;
   auto run = [&](auto clamp_tag) {
     constexpr bool CLAMP = decltype(clamp_tag)::value;
-    for (int32_t s0 = 0; s0 < ns; s0 += GNSB) {
-      if (s0 > 0) {
-#pragma unroll
-        for (int j = 0; j < GNSB; ++j)
-          if (s0 + j < ns) load_raw<FMT>(raw[j], W, s0 + j);
+    for (int64_t ms = 0; ms < m_total; ms += pass_rows) {
+      const int32_t M = (int32_t)(m_total - ms < pass_rows ? m_total - ms : pass_rows);
+      if (ms > 0) __syncthreads();  // the previous pass's LDS reads and sums are done
+      if constexpr (MODE != MODE_DENSE) {
+        if (tid < M) {
+          const int32_t pr = args.sorted_pairs[m_base + ms + tid];
+          s_row[tid] = MODE == MODE_GATEUP ? pr / args.topk : pr;
+        }
+        __syncthreads();
       }
+      // Staged in rounds of XB blocks per thread (64 KiB per round).  Block b =
+      // row r, column block c.  r = trunc((b + 1/2) * fl(1 / bpr)) in fp32 is floor(b / bpr):
+      // the exact quotient lies at least 1 / (2 bpr) from an integer, and the fp32 error, a few
+      // ulp of a value below 2^9 (b < 16384, bpr >= 32), stays far below that margin.
+      const int32_t nblk = M * bpr;
+      for (int32_t base = 0; base < nblk; base += XB * NT) {
+        auto split = [&](int i, int32_t& r, int32_t& c) {
+          const int32_t b = base + tid + NT * i;
+          r = (int32_t)(((float)b + 0.5f) * inv);
+          c = b - r * bpr;
+        };
+        u32x4 xr[XB];
 #pragma unroll
-      for (int j = 0; j < GNSB; ++j) {
-        const int32_t st = s0 + j;
-        if (st >= ns) break;
-        // this lane's first column of the step inside its part; past the part it reads zeros
-        const bool inside = st * SSK + kb * WPL < Kpp;
-        step_mma<FMT, 1, CLAMP>(raw[j], W, cs24, fin24, mzp24,
-                                inside ? arow + st * SSK * 2 : zero_blk, 0, acc);
+        for (int i = 0; i < XB; ++i) {
+          int32_t r, c;
+          split(i, r, c);
+          if (r < M) {
+            int64_t src = ms + r;  // dense x row / MoE h row (sorted pair order)
+            if constexpr (MODE == MODE_GATEUP) src = s_row[r];
+            else if constexpr (MODE == MODE_DOWN) src = m_base + ms + r;
+            xr[i] = *reinterpret_cast<const u32x4*>(args.a + src * args.a_stride + (int64_t)c * 8);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < XB; ++i) {
+          int32_t r, c;
+          split(i, r, c);
+          if (r < M) *reinterpret_cast<u32x4*>(lds_raw + r * pitch + c * 16) = xr[i];
+        }
+      }
+      if (tid < 8) reinterpret_cast<u32x4*>(zero_blk)[tid] = (u32x4){0, 0, 0, 0};
+      __syncthreads();
+
+      const uint8_t* arow = lds_raw + (nl < M ? nl : 0) * pitch + (part * Kpp + kb * WPL) * 2;
+      f32x4 acc[1] = {(f32x4){0.f, 0.f, 0.f, 0.f}};
+      for (int32_t s0 = 0; s0 < ns; s0 += GNSB) {
+        if (s0 > 0 || (ms > 0 && ns > GNSB)) {  // a later block, or block 0 again
+#pragma unroll
+          for (int j = 0; j < GNSB; ++j)
+            if (s0 + j < ns) load_raw<FMT>(raw[j], W, s0 + j);
+        }
+#pragma unroll
+        for (int j = 0; j < GNSB; ++j) {
+          const int32_t st = s0 + j;
+          if (st >= ns) break;
+          // this lane's first column of the step inside its part; past the part it reads zeros
+          const bool inside = st * SSK + kb * WPL < Kpp;
+          step_mma<FMT, 1, CLAMP>(raw[j], W, cs24, fin24, mzp24,
+                                  inside ? arow + st * SSK * 2 : zero_blk, 0, acc);
+        }
+      }
+
+      // K parts summed in order by wave 0 (gate+up: gate parts, then up parts), which writes the
+      // rows 4 kb + i of its column.
+      __syncthreads();
+      f32x4* red = reinterpret_cast<f32x4*>(lds_raw);
+      if (kw > 0) red[(kw - 1) * 64 + lane] = acc[0];
+      __syncthreads();
+      if (kw == 0 && nvalid) {
+        f32x4 g = acc[0];
+#pragma unroll
+        for (int p = 1; p < KP; ++p) g += red[(p - 1) * 64 + lane];
+        f32x4 u = g;
+        if constexpr (MODE == MODE_GATEUP) {
+          u = red[(KP - 1) * 64 + lane];
+#pragma unroll
+          for (int p = 1; p < KP; ++p) u += red[(KP - 1 + p) * 64 + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * kb + i;
+          if (m >= M) continue;
+          if constexpr (MODE == MODE_DENSE) {
+            uint16_t* y = reinterpret_cast<uint16_t*>(args.out);
+            y[(ms + m) * args.out_stride + nrow] = (uint16_t)f32_to_bf16_bits(g[i]);
+          } else if constexpr (MODE == MODE_GATEUP) {
+            uint16_t* h = reinterpret_cast<uint16_t*>(args.out);
+            h[(m_base + ms + m) * args.out_stride + nrow] =
+                (uint16_t)f32_to_bf16_bits(silu_f32(g[i]) * u[i]);
+          } else {
+            float* d = reinterpret_cast<float*>(args.out);
+            d[(int64_t)s_row[m] * args.out_stride + nrow] = g[i];
+          }
+        }
       }
     }
   };
@@ -589,62 +652,58 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const SkinnyArgs args) {
     run(std::integral_constant<bool, false>{});
   else
     run(std::integral_constant<bool, true>{});
-
-  // K parts summed in order by wave 0, which writes the rows 4 kb + i of its column.
-  __syncthreads();
-  f32x4* red = reinterpret_cast<f32x4*>(lds_raw);
-  if (kw > 0) red[(kw - 1) * 64 + lane] = acc[0];
-  __syncthreads();
-  if (kw == 0 && nvalid) {
-#pragma unroll
-    for (int p = 1; p < KS; ++p) acc[0] += red[(p - 1) * 64 + lane];
-    uint16_t* y = reinterpret_cast<uint16_t*>(args.out);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * kb + i;
-      if (m < M) y[(int64_t)m * args.out_stride + nrow] = (uint16_t)f32_to_bf16_bits(acc[0][i]);
-    }
-  }
 }
 
-template <int FMT, int KS>
-hipError_t launch_gemv_ks(const SkinnyArgs& a, size_t lds_bytes, hipStream_t s) {
+template <int FMT, int KS, int MODE>
+hipError_t launch_gemv_ks(const SkinnyArgs& a, int64_t gy, int32_t pass_rows, hipStream_t s) {
   static std::atomic<uint64_t> lds_set{0};  // per instantiation, one bit per device
-  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, KS>),
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<FMT, KS, MODE>),
                                     GEMV_LDS_MAX, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_kernel<FMT, KS>), dim3((unsigned)((a.N + 15) / 16)), dim3(64 * KS),
-                     lds_bytes, s, a);
+  int64_t lds = (int64_t)pass_rows * (2 * a.K + 16) + 128;
+  if (lds < (KS - 1) * 1024) lds = (KS - 1) * 1024;  // the K-part sums reuse it
+  hipLaunchKernelGGL((gemv_kernel<FMT, KS, MODE>), dim3((unsigned)((a.N + 15) / 16), (unsigned)gy),
+                     dim3(64 * KS), (size_t)lds, s, a, pass_rows);
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_gemv_fmt(const SkinnyArgs& a, int ks, size_t lds_bytes, hipStream_t s) {
-  return ks == 16 ? launch_gemv_ks<FMT, 16>(a, lds_bytes, s) : launch_gemv_ks<FMT, 4>(a, lds_bytes, s);
+hipError_t launch_gemv_fmt(int mode, const SkinnyArgs& a, int ks, int64_t gy, int32_t pass_rows,
+                           hipStream_t s) {
+  if constexpr (is_alg2(FMT)) {  // a whole-group decode needs more registers than 16 waves leave
+    if (mode == MODE_GATEUP) return launch_gemv_ks<FMT, 4, MODE_GATEUP>(a, gy, pass_rows, s);
+    if (mode == MODE_DOWN) return launch_gemv_ks<FMT, 4, MODE_DOWN>(a, gy, pass_rows, s);
+    return launch_gemv_ks<FMT, 4, MODE_DENSE>(a, gy, pass_rows, s);
+  } else {
+    if (mode == MODE_GATEUP)
+      return ks == 16 ? launch_gemv_ks<FMT, 16, MODE_GATEUP>(a, gy, pass_rows, s)
+                      : launch_gemv_ks<FMT, 4, MODE_GATEUP>(a, gy, pass_rows, s);
+    if (mode == MODE_DOWN)
+      return ks == 16 ? launch_gemv_ks<FMT, 16, MODE_DOWN>(a, gy, pass_rows, s)
+                      : launch_gemv_ks<FMT, 4, MODE_DOWN>(a, gy, pass_rows, s);
+    return ks == 16 ? launch_gemv_ks<FMT, 16, MODE_DENSE>(a, gy, pass_rows, s)
+                    : launch_gemv_ks<FMT, 4, MODE_DENSE>(a, gy, pass_rows, s);
+  }
 }
 
-template <int FMT, int MT, int MODE, int KSPLIT, int KCB = KCT_BASE>
+template <int FMT, int MT, int MODE, int KSPLIT>
 hipError_t launch_one(const SkinnyArgs& a, int64_t gy, int64_t gz, hipStream_t s) {
-  constexpr int KCT = chunk_cols<FMT, KSPLIT, KCB>() * KSPLIT;
+  constexpr int KCT = chunk_cols<FMT, KSPLIT>() * KSPLIT;
   constexpr size_t lds_bytes = 2 * (size_t)(MT * 16) * (KCT * 2 + 16);
   constexpr int TPW = (KSPLIT == 4) ? 1 : (MODE == MODE_GATEUP ? 2 : 4);
   static std::atomic<uint64_t> lds_set{0};  // per instantiation, one bit per device
   hipError_t e = ensure_dynamic_lds(
-      reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, MODE, KSPLIT, KCB>), (int)lds_bytes, lds_set);
+      reinterpret_cast<const void*>(&skinny_kernel<FMT, MT, MODE, KSPLIT>), (int)lds_bytes, lds_set);
   if (e != hipSuccess) return e;
   const int64_t ntiles = (a.N + 15) / 16;
   dim3 grid((unsigned)((ntiles + TPW - 1) / TPW), (unsigned)gy, (unsigned)gz);
-  hipLaunchKernelGGL((skinny_kernel<FMT, MT, MODE, KSPLIT, KCB>), grid, dim3(256), lds_bytes, s, a);
+  hipLaunchKernelGGL((skinny_kernel<FMT, MT, MODE, KSPLIT>), grid, dim3(256), lds_bytes, s, a);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_fmt(int mode, int mt, int ksplit, const SkinnyArgs& a, int64_t gy, int64_t gz,
-                      hipStream_t s, int chunk) {
-  if (chunk == 2048 && mt == 1 && mode == MODE_GATEUP)
-    return launch_one<FMT, 1, MODE_GATEUP, 1, 2048>(a, gy, gz, s);
-  if (chunk == 2048 && mt == 1 && mode == MODE_DOWN)
-    return launch_one<FMT, 1, MODE_DOWN, 1, 2048>(a, gy, gz, s);
+                      hipStream_t s) {
   if (mode == MODE_DENSE) {
     if (ksplit == 4)
       return mt == 1 ? launch_one<FMT, 1, MODE_DENSE, 4>(a, gy, gz, s)
@@ -659,32 +718,53 @@ hipError_t launch_fmt(int mode, int mt, int ksplit, const SkinnyArgs& a, int64_t
                  : launch_one<FMT, 2, MODE_DOWN, 1>(a, gy, gz, s);
 }
 
-}  // namespace
-
-hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
-                         int64_t grid_y, int64_t grid_z, hipStream_t stream, int chunk) {
+hipError_t dispatch_gemv(int fmt, int mode, const SkinnyArgs& args, int ks, int64_t gy,
+                         int32_t pass_rows, hipStream_t stream) {
   switch (fmt) {
     case FMT_INT4:
-      if (args.w0.group == 0)
-        return launch_fmt<FMT_INT4PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
-      return launch_fmt<FMT_INT4>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
-    case FMT_AFFINE2:
-      return launch_fmt<FMT_AFFINE2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
+      if (args.w0.group == 0) return launch_gemv_fmt<FMT_INT4PC>(mode, args, ks, gy, pass_rows, stream);
+      return launch_gemv_fmt<FMT_INT4>(mode, args, ks, gy, pass_rows, stream);
+    case FMT_AFFINE2: return launch_gemv_fmt<FMT_AFFINE2>(mode, args, ks, gy, pass_rows, stream);
     case FMT_INT8:
-      if (args.w0.group == 0)
-        return launch_fmt<FMT_INT8PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
-      return launch_fmt<FMT_INT8>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
-    case FMT_CCQ432:
-      return launch_fmt<FMT_CCQ432>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
-    case FMT_CCQH:
-      return launch_fmt<FMT_CCQH>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
-    default: return launch_fmt<FMT_CCQ2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream, chunk);
+      if (args.w0.group == 0) return launch_gemv_fmt<FMT_INT8PC>(mode, args, ks, gy, pass_rows, stream);
+      return launch_gemv_fmt<FMT_INT8>(mode, args, ks, gy, pass_rows, stream);
+    case FMT_CCQ432: return launch_gemv_fmt<FMT_CCQ432>(mode, args, ks, gy, pass_rows, stream);
+    case FMT_CCQH: return launch_gemv_fmt<FMT_CCQH>(mode, args, ks, gy, pass_rows, stream);
+    default: return launch_gemv_fmt<FMT_CCQ2>(mode, args, ks, gy, pass_rows, stream);
   }
 }
 
+}  // namespace
+
+hipError_t launch_skinny(int fmt, int mode, int m_tiles, int ksplit, const SkinnyArgs& args,
+                         int64_t grid_y, int64_t grid_z, hipStream_t stream) {
+  switch (fmt) {
+    case FMT_INT4:
+      if (args.w0.group == 0)
+        return launch_fmt<FMT_INT4PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+      return launch_fmt<FMT_INT4>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_AFFINE2:
+      return launch_fmt<FMT_AFFINE2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_INT8:
+      if (args.w0.group == 0)
+        return launch_fmt<FMT_INT8PC>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+      return launch_fmt<FMT_INT8>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_CCQ432:
+      return launch_fmt<FMT_CCQ432>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    case FMT_CCQH:
+      return launch_fmt<FMT_CCQH>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+    default: return launch_fmt<FMT_CCQ2>(mode, m_tiles, ksplit, args, grid_y, grid_z, stream);
+  }
+}
+
+int gemv_pass_rows(int64_t k) {
+  if (k <= 0 || k % 256 != 0 || k >= (1ll << 30)) return 0;
+  const int64_t r = (GEMV_LDS_MAX - 128) / (2 * k + 16);
+  return (int)(r > 16 ? 16 : r);
+}
+
 bool gemv_fits(int64_t m, int64_t n, int64_t k) {
-  return m >= 1 && m <= 16 && k % 256 == 0 && k < (1ll << 30) && (n + 15) / 16 <= 0x7FFFFFFF &&
-         m * (2 * k + 16) + 128 <= GEMV_LDS_MAX;
+  return m >= 1 && m <= gemv_pass_rows(k) && (n + 15) / 16 <= 0x7FFFFFFF;
 }
 
 hipError_t launch_gemv(int fmt, const SkinnyArgs& args, hipStream_t stream) {
@@ -692,21 +772,29 @@ hipError_t launch_gemv(int fmt, const SkinnyArgs& args, hipStream_t stream) {
   // 16 waves per output tile when 4 would leave at least half of the 1024 SIMDs idle (each
   // part a multiple of 64 columns); with 8 the compiler runs out of registers
   const int64_t ntiles = (args.N + 15) / 16;
-  const int ks = (ntiles * 16 <= 2048 && args.K % 1024 == 0) ? 16 : 4;
-  int64_t lds = args.M * (2 * args.K + 16) + 128;
-  if (lds < (ks - 1) * 1024) lds = (ks - 1) * 1024;  // the K-part sums reuse it
-  switch (fmt) {
-    case FMT_INT4:
-      if (args.w0.group == 0) return launch_gemv_fmt<FMT_INT4PC>(args, ks, lds, stream);
-      return launch_gemv_fmt<FMT_INT4>(args, ks, lds, stream);
-    case FMT_AFFINE2: return launch_gemv_fmt<FMT_AFFINE2>(args, ks, lds, stream);
-    case FMT_INT8:
-      if (args.w0.group == 0) return launch_gemv_fmt<FMT_INT8PC>(args, ks, lds, stream);
-      return launch_gemv_fmt<FMT_INT8>(args, ks, lds, stream);
-    case FMT_CCQ432: return launch_gemv_fmt<FMT_CCQ432>(args, ks, lds, stream);
-    case FMT_CCQH: return launch_gemv_fmt<FMT_CCQH>(args, ks, lds, stream);
-    default: return launch_gemv_fmt<FMT_CCQ2>(args, ks, lds, stream);
-  }
+  const int ks = (ntiles * 16 <= 2048 && args.K % 1024 == 0 && !is_alg2(fmt)) ? 16 : 4;
+  return dispatch_gemv(fmt, MODE_DENSE, args, ks, 1, (int32_t)args.M, stream);
+}
+
+int gemv_moe_split(int fmt, int mode, int64_t active_experts, int64_t n, int64_t k) {
+  const int nmat = mode == MODE_GATEUP ? 2 : 1;
+  if (gemv_pass_rows(k) < 1 || k % (64 * (4 / nmat)) != 0) return 0;
+  // at most one workgroup per CU: beyond that (4 tokens of the 256-expert layer, 1024
+  // workgroups) the chunked kernel's four workgroups per CU measured faster
+  const int64_t wgs = active_experts * ((n + 15) / 16);
+  if (wgs > 256) return 0;
+  return (k % (64 * (16 / nmat)) == 0 && !is_alg2(fmt)) ? 16 : 4;
+}
+
+hipError_t launch_gemv_moe(int fmt, int mode, const SkinnyArgs& args, int64_t experts, int ks,
+                           hipStream_t stream) {
+  const int nmat = mode == MODE_GATEUP ? 2 : 1;
+  const int rows = gemv_pass_rows(args.K);
+  if ((mode != MODE_GATEUP && mode != MODE_DOWN) || (ks != 4 && ks != 16) || rows < 1 ||
+      (ks == 16 && is_alg2(fmt)) ||
+      args.K % (64 * (ks / nmat)) != 0 || experts < 1 || experts > 65535)
+    return hipErrorInvalidValue;
+  return dispatch_gemv(fmt, mode, args, ks, experts, rows, stream);
 }
 
 }  // namespace wq
