@@ -779,11 +779,10 @@ hipError_t launch_gemv(int fmt, const SkinnyArgs& args, hipStream_t stream) {
 int gemv_moe_split(int fmt, int mode, int64_t active_experts, int64_t n, int64_t k) {
   const int nmat = mode == MODE_GATEUP ? 2 : 1;
   if (gemv_pass_rows(k) < 1 || k % (64 * (4 / nmat)) != 0) return 0;
-  // at most one workgroup per CU: beyond that (4 tokens of the 256-expert layer, 1024
-  // workgroups) the chunked kernel's four workgroups per CU measured faster
   const int64_t wgs = active_experts * ((n + 15) / 16);
-  if (wgs > 256) return 0;
-  return (k % (64 * (16 / nmat)) == 0 && !is_alg2(fmt)) ? 16 : 4;
+  const bool ks16 = k % (64 * (16 / nmat)) == 0 && !is_alg2(fmt);
+  if (wgs > (ks16 ? 1024 : 256)) return 0;
+  return ks16 ? 16 : 4;
 }
 
 hipError_t launch_gemv_moe(int fmt, int mode, const SkinnyArgs& args, int64_t experts, int ks,
