@@ -99,7 +99,11 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // once -- the single rounding of the exact (c - z) * s whenever z * s is exact in fp32 (z a
 // power of two -- the CCQ zero point 32 -- or z * s with few enough bits: the 2-bit affine
 // zero point times a bf16 scale, INT4's 8 * s).  So one instruction converts and scales a
-// weight, and 16-bit packed shifts place two codes per dword.  For c == z the result is +0
+// weight, and 16-bit packed shifts place two codes per dword.  A field that lies wholly in
+// bits 0..9 of its half need not be shifted down: masked in place at bit p it reads as the
+// subnormal c * 2^(p - 24), and the scale passed with it is s * 2^(24 - p) (an exact power-of-two
+// rescaling), so the product is again exactly c * s.  Only fields reaching into the f16
+// exponent bits (10..14) or the sign bit are shifted.  For c == z the result is +0
 // where the two-step form gives 0 * s: the same bits for s >= 0 (scales are non-negative).
 // For s == 0 (a zero group-scale field) and c < z the two-step form gives -0 and this one +0;
 // no product can tell them apart (every accumulation starts at +0).
@@ -137,6 +141,7 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, f
 #pragma unroll
   for (int b = 0; b < 4; ++b)
     if (CLAMP) t[b] = __builtin_amdgcn_fmed3f(t[b], 0.0f, 32767.0f);
+  const float s21 = s24 * 0.125f;
   float r[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -148,18 +153,19 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, f
         "src1_sel:DWORD"
         : "+v"(P)
         : "v"(t[2 * h + 1]), "v"(12582912.0f));
-    // bit-shift decode: 6-bit states at shifts 9, 6, 3, 0 of each half
+    // bit-shift decode: 6-bit states at shifts 9, 6, 3, 0 of each half; the state at shift 3
+    // (bits 3..8) is read in place with the scale s * 2^21
     const uint32_t q0 = pk_shr16(P, 9);  // C < 2^15: no bits above the field
     const uint32_t q1 = pk_shr16(P, 6) & 0x003F003Fu;
-    const uint32_t q2 = pk_shr16(P, 3) & 0x003F003Fu;
+    const uint32_t q2 = P & 0x01F801F8u;
     const uint32_t q3 = P & 0x003F003Fu;
     r[8 * h + 0] = mix_lo(q0, s24, mzs);
     r[8 * h + 1] = mix_lo(q1, s24, mzs);
-    r[8 * h + 2] = mix_lo(q2, s24, mzs);
+    r[8 * h + 2] = mix_lo(q2, s21, mzs);
     r[8 * h + 3] = mix_lo(q3, s24, mzs);
     r[8 * h + 4] = mix_hi(q0, s24, mzs);
     r[8 * h + 5] = mix_hi(q1, s24, mzs);
-    r[8 * h + 6] = mix_hi(q2, s24, mzs);
+    r[8 * h + 6] = mix_hi(q2, s21, mzs);
     r[8 * h + 7] = mix_hi(q3, s24, mzs);
   }
 #pragma unroll
@@ -168,19 +174,21 @@ __device__ __forceinline__ void ccq_decode16(uint32_t w, float cs24, float cz, f
 
 // INT4: two dwords = 16 signed nibbles (first weight in the low nibble).  XOR 8 biases a
 // two's-complement nibble q to q + 8 in 0..15, so value = fl((q + 8) * s - 8 s);
-// s24 = s * 2^24, m8s = -8 s.
+// s24 = s * 2^24, m8s = -8 s.  The second nibble of each half (bits 4..7) is read in place
+// with the scale s * 2^20.
 __device__ __forceinline__ void int4_decode16(uint32_t w0, uint32_t w1, float s24, float m8s,
                                               uint32_t (&p)[8]) {
+  const float sc[4] = {s24, s24 * 0.0625f, s24, s24};
   float r[16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t d = (h ? w1 : w0) ^ 0x88888888u;  // halves: nibbles 0..3 and 4..7
-    const uint32_t q[4] = {d & 0x000F000Fu, pk_shr16(d, 4) & 0x000F000Fu,
-                           pk_shr16(d, 8) & 0x000F000Fu, pk_shr16(d, 12)};
+    const uint32_t q[4] = {d & 0x000F000Fu, d & 0x00F000F0u, pk_shr16(d, 8) & 0x000F000Fu,
+                           pk_shr16(d, 12)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r[8 * h + i] = mix_lo(q[i], s24, m8s);
-      r[8 * h + 4 + i] = mix_hi(q[i], s24, m8s);
+      r[8 * h + i] = mix_lo(q[i], sc[i], m8s);
+      r[8 * h + 4 + i] = mix_hi(q[i], sc[i], m8s);
     }
   }
 #pragma unroll
@@ -207,18 +215,22 @@ __device__ __forceinline__ void int8_decode16(const u32x4& w, float s24, float m
 }
 
 // 2-bit affine: one dword = 16 codes (first in the lowest two bits); value = fl(q s - z s)
-// with z s exact (8-bit z times a bf16 scale); s24 = s * 2^24, mzs = -z s.
+// with z s exact (8-bit z times a bf16 scale); s24 = s * 2^24, mzs = -z s.  Codes 0..4 of each
+// half (bits 0..9) are read in place at bit 2i with the scale s * 2^(24 - 2i); codes 5..7 are
+// read at bits 4, 6, 8 of the half shifted right by 6.
 __device__ __forceinline__ void affine2_decode16(uint32_t w, float s24, float mzs,
                                                  uint32_t (&p)[8]) {
-  uint32_t q[8];  // q[i]: codes i (low half) and 8 + i (high half)
-#pragma unroll
-  for (int i = 0; i < 7; ++i) q[i] = pk_shr16(w, (uint16_t)(2 * i)) & 0x00030003u;
-  q[7] = pk_shr16(w, 14);
+  const float sc[5] = {s24, s24 * 0.25f, s24 * 0.0625f, s24 * 0.015625f, s24 * 0.00390625f};
+  const uint32_t t = pk_shr16(w, 6);
+  // q[i]: codes i (low half) and 8 + i (high half)
+  const uint32_t q[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u,
+                         w & 0x03000300u, t & 0x00300030u, t & 0x00C000C0u, t & 0x03000300u};
+  const int si[8] = {0, 1, 2, 3, 4, 2, 3, 4};
   float r[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    r[i] = mix_lo(q[i], s24, mzs);
-    r[8 + i] = mix_hi(q[i], s24, mzs);
+    r[i] = mix_lo(q[i], sc[si[i]], mzs);
+    r[8 + i] = mix_hi(q[i], sc[si[i]], mzs);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) p[j] = cvt_pk_bf16(r[2 * j], r[2 * j + 1]);
@@ -230,28 +242,31 @@ __device__ __forceinline__ void affine2_decode16(uint32_t w, float s24, float mz
 // so -zp * s is exact).  s = fl(s_q * super) is formed as fl(s_q * fin24) = s * 2^24 exactly.
 //
 // (4,3,2): byte b (< 21) holds weights 3b, 3b+1, 3b+2 as its states at shifts 4, 2, 0; byte 21
-// holds weight 63 in its high nibble and s_q in its low nibble.  Packed 16-bit shifts decode
-// bytes 4d, 4d+2 (even halves) and 4d+1, 4d+3 (odd halves) of each dword together.
+// holds weight 63 in its high nibble and s_q in its low nibble.  Each 16-bit half of a dword
+// holds bytes 4d, 4d+1 (low) and 4d+2, 4d+3 (high): the even byte's states are read in place
+// (bits 4, 2, 0 of the half), the odd byte's at bits 6, 4, 2 of the half shifted right by 6.
 __device__ __forceinline__ void ccq432_decode64(const uint32_t (&c)[6], float fin24, float mzp24,
                                                 uint32_t (&p)[32]) {
   const float s24 = (float)((c[5] >> 8) & 0xFu) * fin24;
   const float mzs = s24 * mzp24;
+  const float s22 = s24 * 0.25f, s20 = s24 * 0.0625f, s18 = s24 * 0.015625f;
   float v[66];
 #pragma unroll
   for (int d = 0; d < 6; ++d) {
 #pragma unroll
     for (int odd = 0; odd < 2; ++odd) {
-      const uint32_t x = odd ? pk_shr16(c[d], 8) : (c[d] & 0x00FF00FFu);
+      const uint32_t x = odd ? pk_shr16(c[d], 6) : c[d];  // the byte at bit 2 odd, 0 even
       const int b = 4 * d + odd;  // byte in the low half; b + 2 in the high half
-      const uint32_t q0 = pk_shr16(x, 4);  // x < 256 per half: no bits above the state
-      const uint32_t q1 = pk_shr16(x, 2) & 0x000F000Fu;
-      const uint32_t q2 = x & 0x000F000Fu;
-      if (3 * b < 64) v[3 * b] = mix_lo(q0, s24, mzs);
-      if (3 * b + 1 < 64) v[3 * b + 1] = mix_lo(q1, s24, mzs);
-      if (3 * b + 2 < 64) v[3 * b + 2] = mix_lo(q2, s24, mzs);
-      if (3 * b + 6 < 64) v[3 * b + 6] = mix_hi(q0, s24, mzs);
-      if (3 * b + 7 < 64) v[3 * b + 7] = mix_hi(q1, s24, mzs);
-      if (3 * b + 8 < 64) v[3 * b + 8] = mix_hi(q2, s24, mzs);
+      const uint32_t q0 = x & (odd ? 0x03C003C0u : 0x00F000F0u);
+      const uint32_t q1 = x & (odd ? 0x00F000F0u : 0x003C003Cu);
+      const uint32_t q2 = x & (odd ? 0x003C003Cu : 0x000F000Fu);
+      const float a0 = odd ? s18 : s20, a1 = odd ? s20 : s22, a2 = odd ? s22 : s24;
+      if (3 * b < 64) v[3 * b] = mix_lo(q0, a0, mzs);
+      if (3 * b + 1 < 64) v[3 * b + 1] = mix_lo(q1, a1, mzs);
+      if (3 * b + 2 < 64) v[3 * b + 2] = mix_lo(q2, a2, mzs);
+      if (3 * b + 6 < 64) v[3 * b + 6] = mix_hi(q0, a0, mzs);
+      if (3 * b + 7 < 64) v[3 * b + 7] = mix_hi(q1, a1, mzs);
+      if (3 * b + 8 < 64) v[3 * b + 8] = mix_hi(q2, a2, mzs);
     }
   }
 #pragma unroll
@@ -260,21 +275,27 @@ __device__ __forceinline__ void ccq432_decode64(const uint32_t (&c)[6], float fi
 
 // Hybrid (3,3,2)+(3,4,2): u16 word j (< 9) holds weights 7j .. 7j+6 as its states at shifts
 // 13, 11, 9, 6, 4, 2, 0; word 9 holds weight 63 at shift 13 and s_q in bits 0..12.  Dword d
-// holds words 2d (low half) and 2d+1 (high half): one packed shift decodes a state of both.
+// holds words 2d (low half) and 2d+1 (high half).  The states at shifts 6, 4, 2, 0 are read in
+// place; those at 13, 11, 9 at bits 6, 4, 2 of the halves shifted right by 7.
 __device__ __forceinline__ void ccqh_decode64(const uint32_t (&c)[5], float fin24, float mzp24,
                                               uint32_t (&p)[32]) {
   const float s24 = (float)((c[4] >> 16) & 0x1FFFu) * fin24;
   const float mzs = s24 * mzp24;
-  constexpr uint16_t sh[7] = {13, 11, 9, 6, 4, 2, 0};
+  // field position in the (shifted) half and the matching scale s * 2^(24 - position)
+  constexpr uint32_t mask[7] = {0x01C001C0u, 0x00700070u, 0x001C001Cu, 0x01C001C0u,
+                                0x00700070u, 0x001C001Cu, 0x00070007u};
+  const float sc[4] = {s24, s24 * 0.25f, s24 * 0.0625f, s24 * 0.015625f};
+  constexpr int si[7] = {3, 2, 1, 3, 2, 1, 0};
   float v[70];
 #pragma unroll
   for (int d = 0; d < 5; ++d) {
+    const uint32_t t = pk_shr16(c[d], 7);
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
-      const uint32_t q = j == 0 ? pk_shr16(c[d], 13) : (pk_shr16(c[d], sh[j]) & 0x00070007u);
+      const uint32_t q = (j < 3 ? t : c[d]) & mask[j];
       const int w = 14 * d + j;
-      if (w < 64) v[w] = mix_lo(q, s24, mzs);
-      if (w + 7 < 64) v[w + 7] = mix_hi(q, s24, mzs);
+      if (w < 64) v[w] = mix_lo(q, sc[si[j]], mzs);
+      if (w + 7 < 64) v[w + 7] = mix_hi(q, sc[si[j]], mzs);
     }
   }
 #pragma unroll
