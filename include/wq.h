@@ -71,7 +71,9 @@
  *     same bits wq_dequantize returns, except that a weight the definition makes -0 (a zero
  *     group scale times a negative state offset) enters the products as +0, which no sum
  *     starting from +0 can tell apart.
- *   - Sizes are element counts (int64).  Device pointers must be 16-byte aligned.
+ *   - Sizes are element counts (int64).  Device pointers must be 16-byte aligned.  The products
+ *     (wq_gemm, wq_moe_*) address one expert's codes and one activation row with 32-bit byte
+ *     offsets: they return WQ_ERR_UNSUPPORTED for k >= 2^30 or an expert's codes of 2 GiB or more.
  */
 #ifndef WQ_H
 #define WQ_H

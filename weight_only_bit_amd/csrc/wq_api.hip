@@ -58,10 +58,13 @@ int64_t row_code_bytes(const wq_weight* w) {
 
 // The product kernels decode CCQ weights as fma(u, s, -zp*s), exact when zp*s is exact: zp
 // must then be zero or a power of two (the formats' zero points are 32, 8 and 4).
-// The product kernels also address one expert's matrix with 32-bit byte offsets.
+// The product kernels also address one expert's matrix, and one activation row, with 32-bit
+// byte offsets.
 wq_status check_product_zp(const wq_weight* w, const char* what) {
   if (is_ccq(w->format) && (w->zp & (w->zp - 1)) != 0)
     return fail(WQ_ERR_UNSUPPORTED, "%s: products need a CCQ zero point of 0 or a power of two", what);
+  if (w->k >= (1ll << 30))
+    return fail(WQ_ERR_UNSUPPORTED, "%s: products need k below 2^30", what);
   const int64_t row_bytes = row_code_bytes(w);
   if (w->n * row_bytes >= (1ll << 31))
     return fail(WQ_ERR_UNSUPPORTED, "%s: one expert's codes must be below 2 GiB", what);

@@ -261,9 +261,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   constexpr int SPC = KCW / SSK;               // steps per wave per chunk
   constexpr int ROWS = MT * 16;
   constexpr int PITCH = KCT * 2 + 16;  // bytes per LDS row
-  constexpr int BLOCKS = ROWS * (KCT / 16);
-  constexpr int BPT = BLOCKS / 256;  // 16-element activation blocks staged per thread
-  static_assert(BPT * 256 == BLOCKS, "staging must divide evenly");
   static_assert(MODE == MODE_DENSE || KSPLIT == 1, "K split is for dense products");
   constexpr int TPW = (KSPLIT == 4) ? 1 : (MODE == MODE_GATEUP ? 2 : 4);  // tiles per workgroup
 
@@ -315,56 +312,68 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
   for (int64_t ms = 0; ms < m_total; ms += ROWS) {
     const int64_t rows_here = (m_total - ms) < ROWS ? (m_total - ms) : ROWS;
 
-    // Source rows of the activation blocks this thread stages (fixed across chunks).  Rows
-    // past rows_here read the pass's first row (their results are never stored), and columns
-    // past the K part read column 0 and are zeroed when stored: every load in the chunk loop is
-    // unconditional, so the compiler's waits before a chunk's decode count exactly the next
-    // chunk's loads and leave them in flight.
-    const uint16_t* srow[BPT];
-    int sblk[BPT], srowi[BPT];
+    // Staging: every wave-wide load brings one 1 KiB segment of one activation row's chunk
+    // (lane l: bytes 16 l .. 16 l + 15), so each load reads through a wave-uniform buffer
+    // resource: base = the row's chunk start, range = the rest of the row.  The chunk advance is
+    // scalar arithmetic and the lane's byte offset is fixed, and bytes past the row's end read
+    // as zeros.  Rows past rows_here read the pass's first row (their results are never
+    // stored).  With a K split, columns past a part's end read the next part's data and are
+    // zeroed when stored.  Every load in the chunk loop is unconditional, so the compiler's
+    // waits before a chunk's decode count exactly the next chunk's loads and leave them in
+    // flight.
+    constexpr int SEGS = KCT / 512;             // 1 KiB segments per row chunk
+    constexpr int LPW = ROWS * SEGS / 4;        // segment loads per wave per chunk
+    static_assert(LPW * 4 == ROWS * SEGS, "segments must divide over the waves");
+    const uint16_t* srow[LPW];  // wave-uniform row pointers
+    int32_t svoff[LPW];         // lane's byte offset in the row chunk (fixed)
+    int32_t skin[LPW];          // lane's column within its K part, minus the chunk start
+    int32_t sidx[LPW];  // source row (dense, down) or sorted-pair index (gate+up)
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int b = tid + 256 * i;
-      const int row = b / (KCT / 16);
-      sblk[i] = b % (KCT / 16);
-      srowi[i] = row;
-      const int64_t r = m_base + ms + (row < rows_here ? row : 0);
-      if constexpr (MODE == MODE_GATEUP)
-        srow[i] = args.a + (int64_t)(args.sorted_pairs[r] / args.topk) * args.a_stride;
-      else
-        srow[i] = args.a + r * args.a_stride;
+    for (int j = 0; j < LPW; ++j) {
+      const int row = (wave * LPW + j) / SEGS;
+      sidx[j] = (int32_t)(m_base + ms + (row < rows_here ? row : 0));
     }
-    // Per 32-byte block, the lanes whose bit 2 is set write their second 16-byte half first,
-    // so the 8 lanes of each LDS write phase cover 8 distinct 16-byte bank groups.
-    const int swp = (lane >> 2) & 1;
-    u32x4 xr[BPT][2];
-    auto stage_load = [&](int c) {
+    if constexpr (MODE == MODE_GATEUP) {
+      int32_t tok[LPW];  // every index load issued before the first is used
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) {
-        const int part = sblk[i] / (KCW / 16);
-        const int32_t kin = c * KCW + (sblk[i] % (KCW / 16)) * 16;
-        const u32x4* p =
-            reinterpret_cast<const u32x4*>(srow[i] + (int64_t)part * Kpp + (kin < Kpp ? kin : 0));
-        xr[i][0] = p[swp];
-        xr[i][1] = p[swp ^ 1];
+      for (int j = 0; j < LPW; ++j) tok[j] = args.sorted_pairs[sidx[j]];
+#pragma unroll
+      for (int j = 0; j < LPW; ++j)
+        srow[j] = args.a + (int64_t)(__builtin_amdgcn_readfirstlane(tok[j]) / args.topk) * args.a_stride;
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) srow[j] = args.a + (int64_t)sidx[j] * args.a_stride;
+    }
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int seg = (wave * LPW + j) % SEGS;
+      const int col = seg * 512 + 8 * lane;  // LDS column of the lane's 8 elements
+      const int part = col / KCW;
+      skin[j] = col % KCW;
+      svoff[j] = (int32_t)((uint32_t)(part * Kpp + skin[j]) * 2u);  // < 2 K
+    }
+    u32x4 xr[LPW];
+    auto stage_load = [&](int c) {
+      const int64_t c0 = (int64_t)c * KCW;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(srow[j] + c0, (args.K - c0) * 2);
+        xr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, svoff[j], 0, 0));
       }
     };
     auto stage_store = [&](int c, int buf) {
-      if ((c + 1) * KCW > Kpp) {  // last chunk of a K part that ends inside it
+      if constexpr (KSPLIT > 1) {
+        if ((c + 1) * KCW > Kpp) {  // last chunk of a K part that ends inside it
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-          const int32_t kin = c * KCW + (sblk[i] % (KCW / 16)) * 16;
-          if (kin >= Kpp) {
-            xr[i][0] = (u32x4){0, 0, 0, 0};
-            xr[i][1] = (u32x4){0, 0, 0, 0};
-          }
+          for (int j = 0; j < LPW; ++j)
+            if (c * KCW + skin[j] >= Kpp) xr[j] = (u32x4){0, 0, 0, 0};
         }
       }
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) {
-        u32x4* d = reinterpret_cast<u32x4*>(&lds[buf][srowi[i] * PITCH + sblk[i] * 32]);
-        d[swp] = xr[i][0];
-        d[swp ^ 1] = xr[i][1];
+      for (int j = 0; j < LPW; ++j) {
+        const int g = wave * LPW + j;
+        *reinterpret_cast<u32x4*>(&lds[buf][(g / SEGS) * PITCH + (g % SEGS) * 1024 + 16 * lane]) =
+            xr[j];
       }
     };
 
