@@ -100,6 +100,7 @@ def _weight(wq, **kw):
     (dict(format=6, scales=None), -1),        # INT8 needs scales
     (dict(format=6, group=32, scales=0x6000), -2),
     (dict(format=7), -2),
+    (dict(n=1, k=1 << 30), -2),               # products address an activation row in 32 bits
 ])
 def test_gemm_rejects_bad_descriptors_without_launch(wq, kw, status):
     L = wq.lib()
