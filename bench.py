@@ -29,10 +29,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_ccq_gateup_moe_decode.json")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the CCQ gate+up kernel from the committed rocprofv3 counter
-    runs (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel sources
-    changed since those counters were taken."""
+def kernel_record():
+    """The committed record of the CCQ gate+up kernel (rocprofv3 counter runs, instruction count
+    of its compiled loop), or None when the kernel sources changed since it was taken."""
     import hashlib
 
     try:
@@ -42,11 +41,36 @@ def measured_traffic():
         for src in rec["kernel_sources"]:
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
-        if h.hexdigest() != rec["kernel_sources_sha256"]:
-            return None
-        return int(rec["traffic_bytes_per_launch"])
+        return rec if h.hexdigest() == rec["kernel_sources_sha256"] else None
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_traffic():
+    """HBM bytes per launch of the CCQ gate+up kernel from the committed rocprofv3 counter
+    runs (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel sources
+    changed since those counters were taken."""
+    rec = kernel_record()
+    return int(rec["traffic_bytes_per_launch"]) if rec and "traffic_bytes_per_launch" in rec else None
+
+
+# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes at the 2.4 GHz peak clock
+# (a 64-lane instruction occupies a SIMD for 4 cycles).
+VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9
+
+
+def alu_roofline(weights_per_launch, launch_s):
+    """The gate+up kernel against the vector-ALU issue roofline: decoded weights per second
+    against the VALU peak divided by the loop's instructions per weight (counted in the
+    compiled gfx950 loop and kept with the kernel record), or None without a current record."""
+    rec = kernel_record()
+    if not rec or "valu_per_weight" not in rec:
+        return None
+    ipw = float(rec["valu_per_weight"])
+    peak = VALU_LANE_OPS_PEAK / ipw / 1e9
+    achieved = weights_per_launch / launch_s / 1e9
+    return {"bound": "alu", "achieved": round(achieved, 1), "peak": round(peak, 1),
+            "unit": "G weights/s", "frac": round(achieved / peak, 4), "valu_per_weight": ipw}
 
 
 def log(*a):
@@ -216,6 +240,8 @@ def main():
     gu_bytes = float(np.mean([touched[l] * (per_expert[l][0] + per_expert[l][1]) for l in ccq_layers])) \
         + T * H * 2 + T * K * I * 2
     gu_gbs = gu_bytes / (gu_avg_ms * 1e-3) / 1e9
+    # weights one CCQ gate+up launch decodes: gate and up rows of the touched experts
+    gu_weights = float(np.mean([touched[l] for l in ccq_layers])) * 2 * I * H if ccq_layers else 0.0
 
     value = step_weight_bytes / (ms_step * 1e-3) / 1e9
     tok_s = T / (ms_step * 1e-3)
@@ -278,7 +304,8 @@ def main():
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if args.wformat == "ccq" else None,
                      "avg_launch_us": round(gu_avg_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": int(gu_bytes)},
+                     "algorithmic_bytes_per_launch": int(gu_bytes),
+                     "alu": alu_roofline(gu_weights, gu_avg_ms * 1e-3) if args.wformat == "ccq" else None},
         "cpu_baseline": cpu,
         "spot_parity_max_rel_err": parity,
     }
