@@ -326,8 +326,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
     static_assert(LPW * 4 == ROWS * SEGS, "segments must divide over the waves");
     const uint16_t* srow[LPW];  // wave-uniform row pointers
     int32_t svoff[LPW];         // lane's byte offset in the row chunk (fixed)
-    int32_t skin[LPW];          // lane's column within its K part, minus the chunk start
-    int32_t sidx[LPW];  // source row (dense, down) or sorted-pair index (gate+up)
+    int32_t skin[LPW];          // lane's column offset inside its K part's chunk
+    int32_t sidx[LPW];          // source row (dense, down) or sorted-pair index (gate+up)
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int row = (wave * LPW + j) / SEGS;
