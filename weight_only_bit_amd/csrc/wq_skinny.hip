@@ -57,16 +57,34 @@ struct Raw {
   u32x2 extra;     // (4,3,2): code bytes 16..23 of the aligned window; hybrid: bytes 16..19
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+// A byte range of one expert's array.  A load at step offset `off` goes through a resource
+// whose base is advanced by `off` (scalar arithmetic) and whose range shrinks by it, so the
+// range check covers the whole offset and a load past the array reads zeros.
+// Sizes are below 2^31 (the host checks one expert's arrays and k), so the range arithmetic is
+// 32-bit and stays on the scalar unit.
+struct BufView {
+  const uint8_t* base;
+  int32_t bytes;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes > 0 ? bytes : 0,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t at(const BufView& b, int32_t off) {
+  return make_rsrc32(b.base + off, b.bytes - off);
+}
+
+__device__ __forceinline__ BufView view(const void* base, int64_t bytes) {
+  return BufView{reinterpret_cast<const uint8_t*>(base), (int32_t)(bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : bytes)};
 }
 
 // Per-wave view of one weight matrix (one expert); loads go through buffer resources, so an
 // offset outside the matrix reads zeros instead of faulting.
 template <int FMT>
 struct WaveW {
-  __amdgpu_buffer_rsrc_t codes, scales, zeros;
+  BufView codes, scales, zeros;
   int32_t row_codes;   // byte offset of this lane's row and 16-weight slice in codes
   int32_t row_scales;  // byte offset of this lane's row in scales / qscale
   int32_t row_zeros;
@@ -86,32 +104,32 @@ __device__ __forceinline__ WaveW<FMT> wave_weight(const DevWeight& w, int64_t e,
   v.cs = v.cz = 0.f;
   v.fin = 1.0f;
   v.row_scales = v.row_zeros = 0;
-  v.zeros = v.scales = make_rsrc(w.codes, 0);
+  v.zeros = v.scales = view(w.codes, 0);
   if constexpr (is_int4(FMT)) {
-    v.codes = make_rsrc(w.codes + e * n * (k / 2), n * (k / 2));
+    v.codes = view(w.codes + e * n * (k / 2), n * (k / 2));
     v.row_codes = (int32_t)(row * (k / 2) + gb * 32 + kb * 16);
     if constexpr (FMT == FMT_INT4) {  // lane kb's 32 weights of step j lie in group gb + 2 j + kb / 2
-      v.scales = make_rsrc(w.scales + e * n * G, n * G * 2);
+      v.scales = view(w.scales + e * n * G, n * G * 2);
       v.row_scales = (int32_t)(row * G * 2 + (gb + (kb >> 1)) * 2);
     } else {
       v.fin = bf16_bits_to_f32(w.scales[e * n + row]);
     }
   } else if constexpr (is_int8(FMT)) {
     // a step is one group: lane kb holds weights 16 kb .. 16 kb + 15 of group gb + j
-    v.codes = make_rsrc(w.codes + e * n * k, n * k);
+    v.codes = view(w.codes + e * n * k, n * k);
     v.row_codes = (int32_t)(row * k + gb * 64 + kb * 16);
     if constexpr (FMT == FMT_INT8) {
-      v.scales = make_rsrc(w.scales + e * n * G, n * G * 2);
+      v.scales = view(w.scales + e * n * G, n * G * 2);
       v.row_scales = (int32_t)(row * G * 2 + gb * 2);
     } else {
       v.fin = bf16_bits_to_f32(w.scales[e * n + row]);
     }
   } else if constexpr (FMT == FMT_AFFINE2) {
-    v.codes = make_rsrc(w.codes + e * n * (k / 4), n * (k / 4));
+    v.codes = view(w.codes + e * n * (k / 4), n * (k / 4));
     v.row_codes = (int32_t)(row * (k / 4) + gb * 16 + kb * 16);  // group gb + 4 j + kb
-    v.scales = make_rsrc(w.scales + e * n * G, n * G * 2);
+    v.scales = view(w.scales + e * n * G, n * G * 2);
     v.row_scales = (int32_t)(row * G * 2 + (gb + kb) * 2);
-    v.zeros = make_rsrc(w.zeros + e * n * G, n * G);
+    v.zeros = view(w.zeros + e * n * G, n * G);
     v.row_zeros = (int32_t)(row * G + gb + kb);
   } else if constexpr (is_alg2(FMT)) {
     // A group is 22 (or 20) bytes: lane kb's group gb + 4 j + kb starts at an even byte.  Loads
@@ -120,16 +138,16 @@ __device__ __forceinline__ WaveW<FMT> wave_weight(const DevWeight& w, int64_t e,
     constexpr int GB = alg2_group_bytes(FMT);
     const uint8_t* eb = w.codes + e * n * G * GB;
     const int64_t lead = (int64_t)(reinterpret_cast<uintptr_t>(eb) & 3u);
-    v.codes = make_rsrc(eb - lead, (lead + n * G * GB + 3) & ~(int64_t)3);
+    v.codes = view(eb - lead, (lead + n * G * GB + 3) & ~(int64_t)3);
     const int64_t off = lead + row * G * GB + (int64_t)(gb + kb) * GB;
     v.qshift = 8u * (uint32_t)(off & 3);
     v.row_codes = (int32_t)(off & ~(int64_t)3);
     v.fin = w.super_scale[e * n + row];
   } else {
     const int64_t qb = (G + 1) / 2;
-    v.codes = make_rsrc(w.codes + e * n * (k / 4), n * (k / 4));
+    v.codes = view(w.codes + e * n * (k / 4), n * (k / 4));
     v.row_codes = (int32_t)(row * (k / 4) + gb * 16 + kb * 16);  // group gb + 4 j + kb
-    v.scales = make_rsrc(w.qscale + e * n * qb, n * qb);
+    v.scales = view(w.qscale + e * n * qb, n * qb);
     v.row_scales = (int32_t)(row * qb + ((gb + kb) >> 1));  // two 4-bit scales per byte
     v.qshift = 4u * (uint32_t)((gb + kb) & 1);
     v.cs = w.code_scale[e * n + row];
@@ -146,24 +164,24 @@ __device__ __forceinline__ void load_raw(Raw<FMT>& r, const WaveW<FMT>& v, int32
   if constexpr (is_alg2(FMT)) {  // a step advances 4 groups: 88 or 80 bytes, dword aligned
     constexpr int STEP = 4 * alg2_group_bytes(FMT);
     r.codes = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(v.codes, v.row_codes, st * STEP, 0));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(at(v.codes, st * STEP), v.row_codes, 0, 0));
     if constexpr (FMT == FMT_CCQ432)
       r.extra = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(v.codes, v.row_codes + 16, st * STEP, 0));
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(at(v.codes, st * STEP), v.row_codes + 16, 0, 0));
     else
-      r.extra.x = __builtin_amdgcn_raw_buffer_load_b32(v.codes, v.row_codes + 16, st * STEP, 0);
+      r.extra.x = __builtin_amdgcn_raw_buffer_load_b32(at(v.codes, st * STEP), v.row_codes + 16, 0, 0);
     return;
   }
-  r.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v.codes, v.row_codes, st * 64, 0));
+  r.codes = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(at(v.codes, st * 64), v.row_codes, 0, 0));
   if constexpr (FMT == FMT_INT8) {
-    r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 2, 0);
+    r.scale = __builtin_amdgcn_raw_buffer_load_b16(at(v.scales, st * 2), v.row_scales, 0, 0);
   } else if constexpr (FMT == FMT_INT4) {
-    r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 4, 0);
+    r.scale = __builtin_amdgcn_raw_buffer_load_b16(at(v.scales, st * 4), v.row_scales, 0, 0);
   } else if constexpr (FMT == FMT_AFFINE2) {
-    r.scale = __builtin_amdgcn_raw_buffer_load_b16(v.scales, v.row_scales, st * 8, 0);
-    r.zero = __builtin_amdgcn_raw_buffer_load_b8(v.zeros, v.row_zeros, st * 4, 0);
+    r.scale = __builtin_amdgcn_raw_buffer_load_b16(at(v.scales, st * 8), v.row_scales, 0, 0);
+    r.zero = __builtin_amdgcn_raw_buffer_load_b8(at(v.zeros, st * 4), v.row_zeros, 0, 0);
   } else if constexpr (FMT == FMT_CCQ2) {
-    r.scale = __builtin_amdgcn_raw_buffer_load_b8(v.scales, v.row_scales, st * 2, 0);
+    r.scale = __builtin_amdgcn_raw_buffer_load_b8(at(v.scales, st * 2), v.row_scales, 0, 0);
   }
 }
 
@@ -354,10 +372,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
     }
     u32x4 xr[LPW];
     auto stage_load = [&](int c) {
-      const int64_t c0 = (int64_t)c * KCW;
+      const int32_t c0 = c * KCW;  // K < 2^30 (checked on the host)
 #pragma unroll
       for (int j = 0; j < LPW; ++j) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(srow[j] + c0, (args.K - c0) * 2);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc32(srow[j] + c0, ((int32_t)args.K - c0) * 2);
         xr[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, svoff[j], 0, 0));
       }
     };
