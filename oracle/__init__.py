@@ -28,7 +28,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1 builds and loads an AddressSanitizer / UndefinedBehaviorSanitizer build
+# instead (the process must preload the ASan runtime; tests/test_oracle_sanitized.py does so).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=undefined"]
 
 INT4, AFFINE2, CCQ, CCQ432, CCQ_HYBRID, INT8 = 1, 2, 3, 4, 5, 6
 CCQ_ZP = 32  # reading: weight zero point 2^(L-1) for L = 6
@@ -42,7 +47,8 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-               "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+               "-ffp-contract=off", "-Wall", "-Wextra", *(_SAN_FLAGS if _SANITIZE else []),
+               "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -99,7 +105,9 @@ def lib():
             "orc_quant_int4": (i32, [vp, i64, i64, i32, vp, vp]),
             "orc_quant_affine2": (i32, [vp, i64, i64, vp, vp, vp]),
             "orc_ccq_search": (ctypes.c_uint32, [vp, ctypes.c_double, i32, vp]),
-            "orc_quant_ccq": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
+            "orc_quant_ccq": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]),
+            "orc_ccq_encode_group": (ctypes.c_double, [vp, ctypes.c_float, ctypes.c_uint32, i32,
+                                                       i32, vp, vp]),
             "orc_quant_alg2": (i32, [vp, i64, i64, i32, i32, i32, vp, vp]),
             "orc_quant_int8": (i32, [vp, i64, i64, i32, vp, vp]),
         }
@@ -238,6 +246,30 @@ def ccq_search(v, scale: float, zp: int = CCQ_ZP):
     return int(code), float(cost[0])
 
 
+def ccq_encode_group(wg, super_scale: float, sq: int, zp: int = CCQ_ZP, update: bool = True):
+    """One 64-weight group of the (6,4,3) encoder: trellis search at fl(sq * super), then
+    (update) the [CCQ] section 3.4 least-squares scale update, kept only when the group error
+    drops.  Returns (codes [16] of 15 bits, final 4-bit scale, group squared error)."""
+    a = _c(wg, np.float32)
+    assert a.size == 64
+    codes = np.zeros(16, np.uint32)
+    sq_out = np.zeros(1, np.uint32)
+    err = lib().orc_ccq_encode_group(_p(a), float(super_scale), int(sq), int(zp), int(bool(update)),
+                                     _p(codes), _p(sq_out))
+    return codes.astype(np.int64), int(sq_out[0]), float(err)
+
+
+# Encoder refinements of the (6,4,3) code-cluster quantizer (bit mask):
+CCQ_REPICK = 1        # re-pick each C' among the row's 256 decodable codes (reading R11)
+CCQ_SCALE_UPDATE = 2  # [CCQ] section 3.4 least-squares group scale update
+
+
+def _ccq_refine_bits(refine) -> int:
+    if isinstance(refine, bool):
+        return CCQ_REPICK | CCQ_SCALE_UPDATE if refine else 0
+    return int(refine)
+
+
 # ---------------------------------------------------------------------------------------------
 # Packed weights
 # ---------------------------------------------------------------------------------------------
@@ -288,8 +320,13 @@ def default_zp(fmt: int) -> int:
     return {CCQ: CCQ_ZP, CCQ432: CCQ432_ZP, CCQ_HYBRID: CCQ_HYBRID_ZP}.get(fmt, CCQ_ZP)
 
 
-def quantize(w, fmt: int, group: int = 64, refine: bool = True, zp: int | None = None) -> Packed:
-    """Quantize fp32 weights [n, k] or [E, n, k] with the oracle's quantizers."""
+def quantize(w, fmt: int, group: int = 64, refine=True, zp: int | None = None,
+             return_full: bool = False):
+    """Quantize fp32 weights [n, k] or [E, n, k] with the oracle's quantizers.
+
+    CCQ: ``refine`` is True (re-pick and scale update), False, or a mask of CCQ_REPICK |
+    CCQ_SCALE_UPDATE; with ``return_full`` the result is (Packed, codes before the cluster
+    u16 [E, n, k/4])."""
     zp = default_zp(fmt) if zp is None else zp
     w = _c(w, np.float32)
     if w.ndim == 2:
@@ -328,13 +365,15 @@ def quantize(w, fmt: int, group: int = 64, refine: bool = True, zp: int | None =
         sup = np.zeros(E * n, np.float32)
         cs = np.zeros(E * n, np.float32)
         cz = np.zeros(E * n, np.float32)
-        rc = lib().orc_quant_ccq(_p(flat), E * n, k, zp, int(bool(refine)), _p(codes), _p(qscale),
-                                 _p(sup), _p(cs), _p(cz))
+        full = np.zeros((E * n, k // 4), np.uint16) if return_full else None
+        rc = lib().orc_quant_ccq(_p(flat), E * n, k, zp, _ccq_refine_bits(refine), _p(codes),
+                                 _p(qscale), _p(sup), _p(cs), _p(cz), _p(full))
         if rc:
             raise ValueError("bad CCQ shape")
-        return Packed(CCQ, n, k, E, 64, codes.reshape(E, n, -1), qscale=qscale.reshape(E, n, -1),
-                      super_scale=sup.reshape(E, n), code_scale=cs.reshape(E, n),
-                      code_zero=cz.reshape(E, n), zp=zp)
+        p = Packed(CCQ, n, k, E, 64, codes.reshape(E, n, -1), qscale=qscale.reshape(E, n, -1),
+                   super_scale=sup.reshape(E, n), code_scale=cs.reshape(E, n),
+                   code_zero=cz.reshape(E, n), zp=zp)
+        return (p, full.reshape(E, n, -1)) if return_full else p
     if fmt in ALG2_GROUP_BYTES:
         codes = np.zeros((E * n, G * ALG2_GROUP_BYTES[fmt]), np.uint8)
         sup = np.zeros(E * n, np.float32)

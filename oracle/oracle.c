@@ -648,19 +648,85 @@ static double ccq_code_cost(uint32_t code, const double* v, double scale, int32_
   return c;
 }
 
+/* Squared error of a group of 64 weights decoded from its 16 codes at scale s:
+ * sum over i = 0..63, in order, of (w_i - (u_i - zp) * s)^2 with u_i the bit-shift state of
+ * weight i ([CCQ] section 3.4, the quantization-error equation of a group). */
+static double ccq_group_error(const float* wg, const uint32_t* codes, double s, int32_t zp) {
+  double e = 0.0;
+  for (int i = 0; i < 64; ++i) {
+    int32_t u = (int32_t)((codes[i / 4] >> (9 - 3 * (i % 4))) & 0x3Fu);
+    double r = (double)wg[i] - (double)(u - zp) * s;
+    e += r * r;
+  }
+  return e;
+}
+
+/* One group of 64 weights of the (6,4,3) configuration:
+ *   1. trellis search (orc_ccq_search) of its 16 vectors at the decode scale fl(sq * super);
+ *   2. update != 0: [CCQ] section 3.4 "Scale Optimization".  With the searched codes fixed,
+ *      the group error sum_i (W_i - W^q_i S)^2 (W^q_i = state - zp, the decoded value) is
+ *      least at S* = sum_i W_i W^q_i / sum_i (W^q_i)^2 (the derivative set to zero, sums over
+ *      i = 0..g-1 in order).  Readings: S* goes through the same 4-bit compression as the
+ *      first scale (sq2 = clip(round(S* / super), 1, 15)); the group is searched again at
+ *      fl(sq2 * super), and the new scale and codes are kept only when the group error
+ *      (ccq_group_error) drops.  One update, no iteration; skipped when S* is not positive.
+ * codes[16] receives the 15-bit codes, *sq_out the group's 4-bit scale; returns the group's
+ * squared error. */
+ORC_API double orc_ccq_encode_group(const float* wg, float super, uint32_t sq, int32_t zp,
+                                    int32_t update, uint32_t* codes, uint32_t* sq_out) {
+  double s = (double)((float)sq * super);
+  for (int c = 0; c < 16; ++c) {
+    double v[4];
+    for (int j = 0; j < 4; ++j) v[j] = (double)wg[4 * c + j];
+    codes[c] = orc_ccq_search(v, s, zp, NULL);
+  }
+  double err = ccq_group_error(wg, codes, s, zp);
+  *sq_out = sq;
+  if (!update) return err;
+  double num = 0.0, den = 0.0;
+  for (int i = 0; i < 64; ++i) {
+    double q = (double)((int32_t)((codes[i / 4] >> (9 - 3 * (i % 4))) & 0x3Fu) - zp);
+    num += (double)wg[i] * q;
+    den += q * q;
+  }
+  if (!(den > 0.0 && num > 0.0)) return err;
+  double sqd = nearbyint((num / den) / (double)super);
+  if (sqd < 1) sqd = 1;
+  if (sqd > 15) sqd = 15;
+  uint32_t sq2 = (uint32_t)sqd;
+  if (sq2 == sq) return err;
+  double s2 = (double)((float)sq2 * super);
+  uint32_t c2[16];
+  for (int c = 0; c < 16; ++c) {
+    double v[4];
+    for (int j = 0; j < 4; ++j) v[j] = (double)wg[4 * c + j];
+    c2[c] = orc_ccq_search(v, s2, zp, NULL);
+  }
+  double e2 = ccq_group_error(wg, c2, s2, zp);
+  if (e2 < err) {
+    memcpy(codes, c2, sizeof(c2));
+    *sq_out = sq2;
+    return e2;
+  }
+  return err;
+}
+
 /* CCQ (6,4,3) with code cluster, per output row (group 64 along k):
  *   1. group scale s_g = absmax_g / (2^(L-1) - 1) = absmax_g / 31            ([CCQ] Alg. 1)
  *   2. scale compression ([CCQ] section 3.4): super = max_g s_g / 15 per row,
  *      s_q = clip(round(s_g / super), 1, 15) (4 bits), decode scale s = s_q * super (fp32)
- *   3. trellis search of every 4-weight vector against the scaled codebook (orc_ccq_search)
+ *   3. trellis search of every 4-weight vector against the scaled codebook, group by group
+ *      (orc_ccq_encode_group); with refine bit 1 (value 2) each group's scale is then
+ *      optimized ([CCQ] section 3.4, "Scale Optimization")
  *   4. code cluster ([CCQ] section 3.3 Eq.): per row, beta = min C, alpha = (max C - min C)/255
  *      (alpha = 1 for a constant row), C' = clip(round((C - beta) / alpha), 0, 255)
- *   5. refine != 0 (reading: the cluster restricts the code space, so re-pick each C' as the
- *      best of the row's 256 decodable codes; decode parity does not depend on it).
- * zp is the weight zero point (reading: 2^(L-1) = 32). */
+ *   5. refine bit 0 (value 1) (reading: the cluster restricts the code space, so re-pick each
+ *      C' as the best of the row's 256 decodable codes; decode parity does not depend on it).
+ * zp is the weight zero point (reading: 2^(L-1) = 32).  full (optional, u16 [n][k/4])
+ * receives the codes of step 3, before the cluster. */
 ORC_API int32_t orc_quant_ccq(const float* w, int64_t n, int64_t k, int32_t zp, int32_t refine,
                               uint8_t* codes, uint8_t* qscale, float* super_scale,
-                              float* code_scale, float* code_zero) {
+                              float* code_scale, float* code_zero, uint16_t* full_out) {
   if (k % 64) return -1;
   int64_t groups = k / 64;
   int64_t qs_bytes = (groups + 1) / 2;
@@ -684,25 +750,25 @@ ORC_API int32_t orc_quant_ccq(const float* w, int64_t n, int64_t k, int32_t zp, 
     if (!(sup > 0.0f)) sup = 1.0f;
     super_scale[r] = sup;
     memset(qscale + r * qs_bytes, 0, (size_t)qs_bytes);
+    uint32_t cmin = 0x7FFF, cmax = 0;
     for (int64_t g = 0; g < groups; ++g) {
       double amax = 0.0;
       for (int i = 0; i < 64; ++i) amax = fmax(amax, fabs((double)row[g * 64 + i]));
       double sqd = nearbyint((amax / 31.0) / (double)sup);
       if (sqd < 1) sqd = 1;
       if (sqd > 15) sqd = 15;
-      uint32_t sq = (uint32_t)sqd;
+      uint32_t sq;
+      uint32_t* gc = full + r * vecs + g * 16;
+      orc_ccq_encode_group(row + g * 64, sup, (uint32_t)sqd, zp, refine & 2, gc, &sq);
       qscale[r * qs_bytes + (g >> 1)] |= (uint8_t)(sq << (4 * (g & 1)));
       sdec[r * groups + g] = (float)sq * sup;
+      for (int c = 0; c < 16; ++c) {
+        if (gc[c] < cmin) cmin = gc[c];
+        if (gc[c] > cmax) cmax = gc[c];
+      }
     }
-    uint32_t cmin = 0x7FFF, cmax = 0;
-    for (int64_t c = 0; c < vecs; ++c) {
-      double v[4];
-      for (int j = 0; j < 4; ++j) v[j] = (double)row[c * 4 + j];
-      uint32_t code = orc_ccq_search(v, (double)sdec[r * groups + (c * 4) / 64], zp, NULL);
-      full[r * vecs + c] = code;
-      if (code < cmin) cmin = code;
-      if (code > cmax) cmax = code;
-    }
+    if (full_out)
+      for (int64_t c = 0; c < vecs; ++c) full_out[r * vecs + c] = (uint16_t)full[r * vecs + c];
     float alpha = (cmax > cmin) ? (float)((double)(cmax - cmin) / 255.0) : 1.0f;
     float beta = (float)cmin;
     code_scale[r] = alpha;
@@ -712,7 +778,7 @@ ORC_API int32_t orc_quant_ccq(const float* w, int64_t n, int64_t k, int32_t zp, 
       if (cp < 0) cp = 0;
       if (cp > 255) cp = 255;
       uint32_t best = (uint32_t)cp;
-      if (refine) {
+      if (refine & 1) {
         double v[4];
         for (int j = 0; j < 4; ++j) v[j] = (double)row[c * 4 + j];
         double s = (double)sdec[r * groups + (c * 4) / 64];
