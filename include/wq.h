@@ -71,9 +71,12 @@
  *     same bits wq_dequantize returns, except that a weight the definition makes -0 (a zero
  *     group scale times a negative state offset) enters the products as +0, which no sum
  *     starting from +0 can tell apart.
+ *   - The products (wq_gemm, wq_moe_gate_up, wq_moe_down, wq_moe_ffn) also require every scale
+ *     to be below 2^100 in magnitude: they rescale it by up to 2^24 on its way into the decode
+ *     (wq_dequantize has no such limit).  Real weights sit many orders of magnitude below it.
  *   - Sizes are element counts (int64).  Device pointers must be 16-byte aligned.  The products
- *     (wq_gemm, wq_moe_*) address one expert's codes and one activation row with 32-bit byte
- *     offsets: they return WQ_ERR_UNSUPPORTED for k >= 2^30 or an expert's codes of 2 GiB or more.
+ *     address one expert's arrays and one activation row with 32-bit byte offsets: they return
+ *     WQ_ERR_UNSUPPORTED for k >= 2^30 or when one expert's codes exceed 2^31 - 24 bytes.
  */
 #ifndef WQ_H
 #define WQ_H
@@ -133,8 +136,18 @@ wq_status wq_dequantize(const wq_weight* w, uint16_t* out, void* stream);
  * which runs the decode kernels at every m (in launches of at most 65535 x 32 rows). */
 wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y, void* stream);
 
-/* Bytes of device workspace wq_moe_route / wq_moe_ffn need for t tokens, top-k routing over
- * `experts` experts, hidden size `hidden` and expert intermediate size `inter`. */
+/* ---- Mixture-of-experts expert FFN --------------------------------------------------------
+ * The pages' deployment is an MoE model whose expert weights are the low-bit ones (FastDeploy
+ * "WINT2 Quantization": supported architecture MoE; the w4w2 layer map quantizes the experts),
+ * and their grouped-GEMM benchmark routes each token to 8 of 256 experts through a grouped
+ * weight-only product of the tokens gathered per expert (CCQ paper, section 5 "Inference
+ * Performance", the grouped-GEMM operator table).  The calls below are that path: routing
+ * groups the (token, slot) pairs by expert, the grouped gate+up product with SiLU(gate) * up,
+ * the grouped down product, and the routing-weighted sum back per token. */
+
+/* Bytes of device workspace wq_moe_ffn needs for t tokens, top-k routing over `experts`
+ * experts, hidden size `hidden` and expert intermediate size `inter` (expert offsets, the
+ * sorted pair list, h and d of the stages below).  0 for invalid sizes. */
 size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t hidden,
                               int64_t inter);
 
@@ -143,7 +156,9 @@ size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t 
  * t*topk); sorted_pairs[expert_offsets[e] ...] lists expert e's pairs in increasing p.
  * topk_ids int32 [t][topk] must lie in [0, experts); the device drops a pair whose id lies
  * outside (it lands in no expert's list and nothing is written out of bounds), and the
- * outputs of its token are then unspecified. */
+ * outputs of its token are then unspecified.  ws and ws_bytes are reserved (routing needs no
+ * workspace): pass NULL and 0, anything else returns WQ_ERR_ARG.  At most 512 experts and
+ * 2^30 pairs. */
 wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t experts,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* ws,
                        size_t ws_bytes, void* stream);
@@ -153,7 +168,12 @@ wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t
  *   h_{t,j} = bf16( SiLU(W_gate[e] x_t) * (W_up[e] x_t) )
  * x bf16 [t][hidden], y bf16 [t][hidden]; gate and up are [E][inter][hidden], down is
  * [E][hidden][inter]; the slot sum runs in order j = 0..topk-1 in fp32.  Routing weights are
- * used as given.  ws must hold wq_moe_workspace_bytes(t, topk, E, hidden, inter) bytes. */
+ * used as given.  ws must hold wq_moe_workspace_bytes(t, topk, E, hidden, inter) bytes (device
+ * memory, caller-owned, nothing in it needs to be initialized).  The expert products are the
+ * weight-only grouped GEMMs of the CCQ paper's section 5 (BF16 activations against the
+ * experts' decoded low-bit weights); SiLU(gate) * up between them is the expert FFN of the
+ * deployed MoE models, with h rounded to bf16 because every product takes BF16 operands
+ * (FastDeploy "WINT2 Quantization": BF16 arithmetic). */
 wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
                      const float* topk_weights, int32_t topk, const wq_weight* gate,
                      const wq_weight* up, const wq_weight* down, uint16_t* y, void* ws,
@@ -161,7 +181,10 @@ wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t
 
 /* The stages of wq_moe_ffn, for callers that route elsewhere or time the stages separately
  * (wq_moe_ffn = wq_moe_route + wq_moe_gate_up + wq_moe_down + wq_moe_combine).  The routing
- * arrays are those wq_moe_route produces; npairs = t * topk.
+ * arrays are those wq_moe_route produces; npairs = t * topk.  wq_moe_gate_up and wq_moe_down
+ * are the two grouped products of the CCQ paper's grouped-GEMM table (section 5; its shapes
+ * "groups x output x input" 256 x 1024 x 7168 are gate+up, two 512-row matrices against a
+ * 7168-wide token, and 256 x 7168 x 512 the down product).
  * wq_moe_gate_up: h[r] = bf16(SiLU(W_gate[e] x_tok) * (W_up[e] x_tok)) for every sorted
  *   position r (expert e, pair p = sorted_pairs[r], token p / topk); h bf16 [npairs][inter].
  * wq_moe_down: d[p] = W_down[e] h[r] in fp32 for every sorted position r, stored by pair id
@@ -176,22 +199,28 @@ wq_status wq_moe_combine(const float* d, const float* topk_weights, int64_t t, i
                          int64_t hidden, uint16_t* y, void* stream);
 
 /* CCQ (6,4,3) code-cluster encoder (CCQ paper, algorithm "Convolutional Code Quantization" of
- * section 3.1, section 3.3 Eq. 1, section 3.4 scale compression): fp32 weights w[n][k] (device,
- * row-major; an MoE tensor is n = experts x rows) -> the WQ_FMT_CCQ2 arrays of the layout above
- * (codes u8[n][k/4], qscale u8[n][(k/64+1)/2], super_scale, code_scale, code_zero f32[n], all
- * device memory owned by the caller).  Per row, groups of 64:
+ * section 3.1, section 3.3 Eq. 1, section 3.4 scale optimization (Eq. 2-4) and scale
+ * compression): fp32 weights w[n][k] (device, row-major; an MoE tensor is n = experts x rows)
+ * -> the WQ_FMT_CCQ2 arrays of the layout above (codes u8[n][k/4], qscale u8[n][(k/64+1)/2],
+ * super_scale, code_scale, code_zero f32[n], all device memory owned by the caller).  Per row,
+ * groups of 64:
  *   s_g = absmax_g / 31; super = f32(max_g s_g / 15) (1 for a zero row);
  *   s_q = clip(round(s_g / super), 1, 15); s = f32(s_q) * super;
  *   C = the 15-bit code minimizing sum_j (v_j - (u_j - zp) s)^2 over the vector's 4 weights
  *       (u_j: states at shifts 9, 6, 3, 0; ties to the smallest code);
+ *   refine bit 1 (value 2), scale optimization: with a group's codes fixed, S* = sum_i w_i q_i /
+ *       sum_i q_i^2 (q_i = u_i - zp over the group's 64 weights in order); when S* > 0 and
+ *       s_q2 = clip(round(S* / super), 1, 15) differs from s_q, the group is searched again at
+ *       f32(s_q2) * super and takes s_q2 and the new codes if its error sum_i (w_i - q_i s)^2
+ *       drops;
  *   beta = min C, alpha = f32((max C - min C) / 255) (1 if all codes are equal);
- *   C' = clip(round((C - beta) / alpha), 0, 255), or, when refine != 0, the C' in 0..255 whose
- *       decoded code (round(fmaf(C', alpha, beta)) clamped to [0, 2^15 - 1]) costs least
- *       (ties to the smallest C').
+ *   C' = clip(round((C - beta) / alpha), 0, 255), or, with refine bit 0 (value 1), the C' in
+ *       0..255 whose decoded code (round(fmaf(C', alpha, beta)) clamped to [0, 2^15 - 1]) costs
+ *       least (ties to the smallest C').
  * Costs, ratios and roundings to integers are taken in fp64 (round half to even), so the
  * outputs are a function of w alone.  Requires k % 64 == 0, k <= 131072 (one workgroup keeps
- * a row's codes in LDS), zp in 0..127, w 16-byte aligned.  Asynchronous on `stream`, no
- * allocation. */
+ * a row's codes in LDS), zp in 0..127, refine in 0..3, w 16-byte aligned.  Asynchronous on
+ * `stream`, no allocation. */
 wq_status wq_quantize_ccq(const float* w, int64_t n, int64_t k, int32_t zp, int32_t refine,
                           uint8_t* codes, uint8_t* qscale, float* super_scale, float* code_scale,
                           float* code_zero, void* stream);

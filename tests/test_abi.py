@@ -156,3 +156,50 @@ def test_quantize_ccq_argument_checks(wq):
     assert call(4, 256, 200) == -2
     assert call(4, 256, 32, w=None) == -1
     assert call(4, 256, 32, w=ctypes.c_void_p(0x10008)) == -3
+    for bad in (-1, 4, 7):                         # refine is a mask of 1 (re-pick) and 2 (scale update)
+        assert L.wq_quantize_ccq(p[0], 4, 256, 32, bad, *p[1:], None) == -1
+
+
+def test_route_workspace_is_reserved(wq):
+    L = wq.lib()
+    ids = ctypes.c_void_p(0x50000)
+    off, pairs = ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000)
+    assert L.wq_moe_route(ids, 4, 2, 8, off, pairs, ctypes.c_void_p(0x80000), 0, None) == -1
+    assert L.wq_moe_route(ids, 4, 2, 8, off, pairs, None, 256, None) == -1
+    assert b"reserved" in L.wq_last_error()
+
+
+def test_products_reject_experts_beyond_the_32bit_buffer_range(wq):
+    """One expert's codes are addressed through 32-bit buffer resources whose range the
+    kernels cap at 0x7FFFFFF0 bytes (plus up to 6 bytes of dword alignment for the (4,3,2) and
+    hybrid views): a larger expert is rejected before any launch instead of reading zeros."""
+    L = wq.lib()
+    x, y = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+    limit = 0x7FFFFFF0 - 8
+    # hybrid, k = 64: 20 bytes per row
+    n_ok, n_bad = limit // 20, limit // 20 + 1
+    for n, want in ((n_bad, -2), (107374182, -2)):  # 107374182 * 20 = 2^31 - 8
+        w = _weight(wq, experts=1, n=n, k=64, format=5, qscale=None, code_scale=None, code_zero=None)
+        assert L.wq_gemm(x, 1, ctypes.byref(w), y, None) == want, n
+        assert b"codes must not exceed" in L.wq_last_error()
+    assert n_ok * 20 <= limit
+    # INT8 per channel: k bytes per row
+    w = _weight(wq, experts=1, n=(limit // 4096) + 1, k=4096, format=6, group=0, scales=0x6000,
+                qscale=None, super_scale=None, code_scale=None, code_zero=None)
+    assert L.wq_gemm(x, 1, ctypes.byref(w), y, None) == -2
+
+
+def test_binding_rejects_host_tensors(wq):
+    import torch
+
+    x = torch.zeros((2, 64), dtype=torch.bfloat16)
+    w = wq.PackedWeight(wq.FMT_INT4, 8, 64, 1, 64, torch.zeros(8 * 32, dtype=torch.uint8),
+                        torch.zeros(8, dtype=torch.int16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        wq.wq_gemm(x, w, y=torch.zeros((2, 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        w.cstruct()
+    assert wq._layout(wq.FMT_CCQ2, 2, 8, 128, 64)["qscale"] == (2 * 8 * 1, 1)
+    assert wq._layout(wq.FMT_INT4, 1, 8, 128, 0)["scales"] == (8, 2)
+    assert wq._layout(wq.FMT_CCQ432, 1, 8, 128, 64)["codes"] == (8 * 2 * 22, 1)
+    assert wq._layout(wq.FMT_INT4, 1, 8, 100, 64) is None

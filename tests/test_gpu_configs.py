@@ -106,13 +106,23 @@ def test_moe_decode_layer_full_size(wq, name):
     mats = _layer(wq, fmt, group, 6300 + fmt)
     x = synth.acts_bf16((32, HIDDEN), 63, 1)
     ids, wts = synth.routing_uniform(32, TOPK, E, 63, 2)
-    _check_tokens(wq, mats, x, ids, wts, np.array([0, 17, 31], np.int32),
+    _check_tokens(wq, mats, x, ids, wts, np.arange(32, dtype=np.int32),
                   f"moe decode full size {name}")
 
 
+def _tile_class(rows):
+    """The tiled kernel's row tile that holds an expert's last rows: its remainder rows % 256
+    goes to one tile of 256, 128, 64 or 32 rows (0: the expert fills whole 256-row tiles)."""
+    rem = rows % 256
+    return 0 if rem == 0 else 256 if rem > 128 else 128 if rem > 64 else 64 if rem > 32 else 32
+
+
 def test_moe_prefill_layer_full_size(wq):
-    # the prefill layer: 4096 tokens, Zipf-skewed top-8 of 64 experts, CCQ g64; sampled tokens
-    # routed to the heaviest expert, to the lightest expert that has rows, and the last token
+    # the prefill layer: 4096 tokens, Zipf-skewed top-8 of 64 experts, CCQ g64.  Sampled tokens
+    # reach every row-tile class: for two experts of each remainder class (256, 128, 64, 32
+    # rows) the token of the expert's first row and of its last row (which lies in the
+    # remainder tile), the heaviest expert's first, middle-tile and last rows, and the last
+    # token.
     _say("moe prefill full size ccq")
     mats = _layer(wq, oracle.CCQ, 64, 6400)
     T = 4096
@@ -120,11 +130,17 @@ def test_moe_prefill_layer_full_size(wq):
     ids, wts = synth.routing_zipf(T, TOPK, E, 64, 2)
     counts = np.bincount(ids.ravel(), minlength=E)
     heavy = int(np.argmax(counts))
-    light = int(np.argmin(np.where(counts > 0, counts, T * TOPK)))
-    assert counts[heavy] > 1024 and counts[light] < 64
-    t_heavy = int(np.nonzero((ids == heavy).any(axis=1))[0][0])
-    t_light = int(np.nonzero((ids == light).any(axis=1))[0][-1])
-    tokens = np.array(sorted({t_heavy, t_light, T - 1}), np.int32)
+    assert counts[heavy] > 1024
+    toks_of = [np.nonzero((ids == e).any(axis=1))[0] for e in range(E)]
+    picked = {T - 1}
+    hv = toks_of[heavy]
+    picked |= {int(hv[0]), int(hv[len(hv) // 2]), int(hv[-1])}
+    for cls in (256, 128, 64, 32):
+        es = [e for e in range(E) if counts[e] and _tile_class(int(counts[e])) == cls]
+        assert len(es) >= 2, (cls, es)
+        for e in es[:2]:
+            picked |= {int(toks_of[e][0]), int(toks_of[e][-1])}
+    tokens = np.array(sorted(picked), np.int32)
     _check_tokens(wq, mats, x, ids, wts, tokens, "moe prefill full size ccq")
 
 

@@ -554,8 +554,11 @@ def test_gemm_ccq_clamped_rows_bit_exact(wq):
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("shape,zp,refine", [((1, 40, 320), 32, True), ((1, 40, 320), 32, False),
+                                             ((1, 40, 320), 32, oracle.CCQ_REPICK),
+                                             ((1, 40, 320), 32, oracle.CCQ_SCALE_UPDATE),
                                              ((2, 24, 1024), 32, True), ((1, 6, 8192), 32, True),
-                                             ((1, 16, 448), 0, True), ((1, 16, 448), 16, False)])
+                                             ((1, 16, 448), 0, True), ((1, 16, 448), 16, False),
+                                             ((1, 3, 131072), 32, True)])
 def test_quantize_ccq_matches_oracle(wq, shape, zp, refine):
     import torch
 

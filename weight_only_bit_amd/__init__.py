@@ -114,6 +114,63 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# ---------------------------------------------------------------------------------------------
+# Argument checks.  The library receives bare device pointers, so it cannot see a tensor's
+# dtype, shape, strides or device; a wrong one would make a kernel read or write out of
+# bounds.  Every wrapper therefore checks its tensors here before the call.
+# ---------------------------------------------------------------------------------------------
+
+def _dtypes():
+    import torch
+
+    return {"bf16": (torch.bfloat16, torch.int16), "i32": (torch.int32,), "f32": (torch.float32,),
+            "u8": (torch.uint8, torch.int8)}
+
+
+def _need(t, name, kind, shape=None, numel=None):
+    """t must be a contiguous tensor of `kind` on the current GPU, of the given shape / size."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: must be on the current GPU (cuda:{torch.cuda.current_device()}), "
+                         f"got {t.device}")
+    if t.dtype not in _dtypes()[kind]:
+        raise TypeError(f"{name}: dtype {t.dtype} is not {kind} ({_dtypes()[kind]})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the layout needs {numel}")
+    return t
+
+
+# Element count and element size of each array a packed weight [E][n][k] holds, per format
+# (include/wq.h layouts); None where the format / group / k combination is not one the
+# library accepts (the library's own status then names the problem).
+def _layout(fmt, E, n, k, group):
+    if k <= 0 or k % 64 or n <= 0 or E <= 0:
+        return None
+    G, rows = k // 64, E * n
+    per_row_scale = rows * (G if group == 64 else 1)
+    if fmt == FMT_INT4 and group in (0, 64):
+        return {"codes": (rows * k // 2, 1), "scales": (per_row_scale, 2)}
+    if fmt == FMT_INT8 and group in (0, 64):
+        return {"codes": (rows * k, 1), "scales": (per_row_scale, 2)}
+    if fmt == FMT_INT2_AFFINE and group == 64:
+        return {"codes": (rows * k // 4, 1), "scales": (rows * G, 2), "zeros": (rows * G, 1)}
+    if fmt == FMT_CCQ2 and group == 64:
+        return {"codes": (rows * k // 4, 1), "qscale": (rows * ((G + 1) // 2), 1),
+                "super_scale": (rows, 4), "code_scale": (rows, 4), "code_zero": (rows, 4)}
+    if fmt in (FMT_CCQ432, FMT_CCQ_HYBRID) and group == 64:
+        return {"codes": (rows * G * (22 if fmt == FMT_CCQ432 else 20), 1), "super_scale": (rows, 4)}
+    return None
+
+
 @dataclass
 class PackedWeight:
     """Device tensors of a packed weight [experts, n, k] (see include/wq.h for layouts)."""
@@ -133,6 +190,24 @@ class PackedWeight:
     _c: object = field(default=None, repr=False)
 
     def cstruct(self) -> _CWeight:
+        """The C descriptor, after checking that every array the format uses is a contiguous
+        tensor on the current GPU with the layout's element size and count."""
+        import torch
+
+        lay = _layout(self.format, self.experts, self.n, self.k, self.group)
+        for name, (numel, size) in (lay or {}).items():
+            t = getattr(self, name)
+            if t is None:
+                raise ValueError(f"PackedWeight.{name}: required by format {self.format}")
+            if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+                raise ValueError(f"PackedWeight.{name}: must be a GPU tensor")
+            if t.device.index != torch.cuda.current_device():
+                raise ValueError(f"PackedWeight.{name}: must be on the current GPU")
+            if not t.is_contiguous():
+                raise ValueError(f"PackedWeight.{name}: must be contiguous")
+            if t.element_size() != size or t.numel() != numel:
+                raise ValueError(f"PackedWeight.{name}: {t.numel()} elements of {t.element_size()} "
+                                 f"bytes, the layout needs {numel} of {size}")
         self._c = _CWeight(self.format, self.group, self.experts, self.n, self.k,
                            *[None if getattr(self, f) is None else getattr(self, f).data_ptr()
                              for f in ("codes", "scales", "zeros", "qscale", "super_scale",
@@ -175,6 +250,7 @@ def wq_dequantize(w: PackedWeight, out=None):
 
     if out is None:
         out = torch.empty((w.experts, w.n, w.k), dtype=torch.int16, device=w.codes.device)
+    _need(out, "wq_dequantize out", "bf16", numel=w.experts * w.n * w.k)
     _check(lib().wq_dequantize(ctypes.byref(w.cstruct()), _ptr(out), _stream()), "wq_dequantize")
     return out
 
@@ -183,9 +259,13 @@ def wq_gemm(x, w: PackedWeight, y=None):
     """y = bf16(x @ dequant(W)^T); x is [m, k] bf16 (torch.bfloat16 or int16 bits)."""
     import torch
 
+    if x.dim() != 2:
+        raise ValueError(f"wq_gemm: x must be [m, k], got shape {tuple(x.shape)}")
     m = x.shape[0]
+    _need(x, "wq_gemm x", "bf16", shape=(m, w.k))
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.bfloat16, device=x.device)
+    _need(y, "wq_gemm y", "bf16", shape=(m, w.n))
     _check(lib().wq_gemm(_ptr(x), m, ctypes.byref(w.cstruct()), _ptr(y), _stream()), "wq_gemm")
     return y
 
@@ -198,7 +278,10 @@ def wq_moe_route(topk_ids, experts: int):
     """(expert_offsets int32 [E+1], sorted_pairs int32 [t*topk]) on the device."""
     import torch
 
+    if topk_ids.dim() != 2:
+        raise ValueError("wq_moe_route: topk_ids must be [t, topk]")
     t, topk = topk_ids.shape
+    _need(topk_ids, "wq_moe_route topk_ids", "i32")
     off = torch.empty(experts + 1, dtype=torch.int32, device=topk_ids.device)
     pairs = torch.empty(t * topk, dtype=torch.int32, device=topk_ids.device)
     _check(lib().wq_moe_route(_ptr(topk_ids), t, topk, experts, _ptr(off), _ptr(pairs), None, 0,
@@ -211,13 +294,20 @@ def wq_moe_ffn(x, topk_ids, topk_weights, gate: PackedWeight, up: PackedWeight,
     """MoE expert FFN; x [t, hidden] bf16, topk_ids int32 [t, topk], topk_weights f32."""
     import torch
 
+    if x.dim() != 2 or topk_ids.dim() != 2:
+        raise ValueError("wq_moe_ffn: x must be [t, hidden] and topk_ids [t, topk]")
     t, hidden = x.shape
     topk = topk_ids.shape[1]
+    _need(x, "wq_moe_ffn x", "bf16")
+    _need(topk_ids, "wq_moe_ffn topk_ids", "i32", shape=(t, topk))
+    _need(topk_weights, "wq_moe_ffn topk_weights", "f32", shape=(t, topk))
     if y is None:
         y = torch.empty((t, hidden), dtype=torch.bfloat16, device=x.device)
+    _need(y, "wq_moe_ffn y", "bf16", shape=(t, hidden))
     need = wq_moe_workspace_bytes(t, topk, gate.experts, hidden, gate.n)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _need(ws, "wq_moe_ffn ws", "u8")
     _check(lib().wq_moe_ffn(_ptr(x), t, hidden, _ptr(topk_ids), _ptr(topk_weights), topk,
                             ctypes.byref(gate.cstruct()), ctypes.byref(up.cstruct()),
                             ctypes.byref(down.cstruct()), _ptr(y), _ptr(ws), ws.numel(),
@@ -230,9 +320,15 @@ def wq_moe_gate_up(x, offsets, sorted_pairs, topk: int, gate: PackedWeight, up: 
     """h [t*topk, inter] bf16 (rows in expert-sorted order) = SiLU(gate x) * (up x)."""
     import torch
 
+    if x.dim() != 2:
+        raise ValueError("wq_moe_gate_up: x must be [t, hidden]")
     t = x.shape[0]
+    _need(x, "wq_moe_gate_up x", "bf16", shape=(t, gate.k))
+    _need(offsets, "wq_moe_gate_up offsets", "i32", numel=gate.experts + 1)
+    _need(sorted_pairs, "wq_moe_gate_up sorted_pairs", "i32", numel=t * topk)
     if h is None:
         h = torch.empty((t * topk, gate.n), dtype=torch.bfloat16, device=x.device)
+    _need(h, "wq_moe_gate_up h", "bf16", shape=(t * topk, gate.n))
     _check(lib().wq_moe_gate_up(_ptr(x), t, _ptr(offsets), _ptr(sorted_pairs), topk,
                                 ctypes.byref(gate.cstruct()), ctypes.byref(up.cstruct()), _ptr(h),
                                 _stream()), "wq_moe_gate_up")
@@ -243,8 +339,12 @@ def wq_moe_down(h, t: int, topk: int, offsets, sorted_pairs, down: PackedWeight,
     """d [t*topk, hidden] f32 (row = pair id) = down h."""
     import torch
 
+    _need(h, "wq_moe_down h", "bf16", shape=(t * topk, down.k))
+    _need(offsets, "wq_moe_down offsets", "i32", numel=down.experts + 1)
+    _need(sorted_pairs, "wq_moe_down sorted_pairs", "i32", numel=t * topk)
     if d is None:
         d = torch.empty((t * topk, down.n), dtype=torch.float32, device=h.device)
+    _need(d, "wq_moe_down d", "f32", shape=(t * topk, down.n))
     _check(lib().wq_moe_down(_ptr(h), t, topk, _ptr(offsets), _ptr(sorted_pairs),
                              ctypes.byref(down.cstruct()), _ptr(d), _stream()), "wq_moe_down")
     return d
@@ -254,23 +354,35 @@ def wq_moe_combine(d, topk_weights, y=None):
     """y [t, hidden] bf16 = sum_j topk_weights[t, j] * d[t*topk + j]."""
     import torch
 
+    if topk_weights.dim() != 2 or d.dim() != 2:
+        raise ValueError("wq_moe_combine: topk_weights must be [t, topk] and d [t*topk, hidden]")
     t, topk = topk_weights.shape
     hidden = d.shape[1]
+    _need(topk_weights, "wq_moe_combine topk_weights", "f32")
+    _need(d, "wq_moe_combine d", "f32", shape=(t * topk, hidden))
     if y is None:
         y = torch.empty((t, hidden), dtype=torch.bfloat16, device=d.device)
+    _need(y, "wq_moe_combine y", "bf16", shape=(t, hidden))
     _check(lib().wq_moe_combine(_ptr(d), _ptr(topk_weights), t, topk, hidden, _ptr(y), _stream()),
            "wq_moe_combine")
     return y
 
 
-def wq_quantize_ccq(w, zp: int = 32, refine: bool = True) -> PackedWeight:
-    """CCQ (6,4,3) code-cluster encoding of fp32 weights [n, k] or [E, n, k] on the GPU."""
+CCQ_REPICK = 1        # wq_quantize_ccq refine bit: re-pick clustered codes among decodable ones
+CCQ_SCALE_UPDATE = 2  # wq_quantize_ccq refine bit: least-squares group scale update
+
+
+def wq_quantize_ccq(w, zp: int = 32, refine=True) -> PackedWeight:
+    """CCQ (6,4,3) code-cluster encoding of fp32 weights [n, k] or [E, n, k] on the GPU.
+    refine: True (re-pick and scale update), False, or a mask of CCQ_REPICK | CCQ_SCALE_UPDATE."""
     import torch
 
     if w.dim() == 2:
         w = w.unsqueeze(0)
+    if w.dim() != 3:
+        raise ValueError("wq_quantize_ccq: w must be [n, k] or [E, n, k]")
     E, n, k = w.shape
-    w = w.contiguous().float()
+    w = _need(w.contiguous().float(), "wq_quantize_ccq w", "f32")
     dev = w.device
     rows = E * n
     G = k // 64
@@ -279,7 +391,8 @@ def wq_quantize_ccq(w, zp: int = 32, refine: bool = True) -> PackedWeight:
     sup = torch.empty((E, n), dtype=torch.float32, device=dev)
     cs = torch.empty((E, n), dtype=torch.float32, device=dev)
     cz = torch.empty((E, n), dtype=torch.float32, device=dev)
-    _check(lib().wq_quantize_ccq(_ptr(w), rows, k, zp, int(bool(refine)), _ptr(codes), _ptr(qscale),
+    mask = (CCQ_REPICK | CCQ_SCALE_UPDATE if refine else 0) if isinstance(refine, bool) else int(refine)
+    _check(lib().wq_quantize_ccq(_ptr(w), rows, k, zp, mask, _ptr(codes), _ptr(qscale),
                                  _ptr(sup), _ptr(cs), _ptr(cz), _stream()), "wq_quantize_ccq")
     return PackedWeight(FMT_CCQ2, n, k, E, 64, codes, None, None, qscale, sup, cs, cz, zp)
 

@@ -21,8 +21,19 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, obj_dir: str) -> str:
+def _headers_mtime() -> float:
+    inc = os.path.join(os.path.dirname(HERE), "include")
+    paths = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    paths += [os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h")]
+    return max(os.path.getmtime(p) for p in paths)
+
+
+def _compile(src: str, obj_dir: str, force: bool = True) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+    if not force and os.path.exists(obj):
+        newest = max(os.path.getmtime(os.path.join(CSRC, src)), _headers_mtime())
+        if os.path.getmtime(obj) >= newest:
+            return obj
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -31,11 +42,12 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, force: bool = True) -> str:
+    """Compile every source (force) or only those older than their source or a header."""
     obj_dir = os.path.join(HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, force), SOURCES))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
@@ -46,4 +58,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, force="--incremental" not in sys.argv)

@@ -56,18 +56,24 @@ int64_t row_code_bytes(const wq_weight* w) {
   }
 }
 
+// Largest byte range of one expert's array that the decode kernels' 32-bit buffer resources
+// cover (the (4,3,2) / hybrid code views add up to 6 bytes of dword alignment to it).
+constexpr int64_t kMaxExpertBytes = 0x7FFFFFF0ll - 8;
+
 // The product kernels decode CCQ weights as fma(u, s, -zp*s), exact when zp*s is exact: zp
 // must then be zero or a power of two (the formats' zero points are 32, 8 and 4).
-// The product kernels also address one expert's matrix, and one activation row, with 32-bit
-// byte offsets.
+// The product kernels also address one expert's arrays, and one activation row, with 32-bit
+// byte offsets: every array of one expert must lie within kMaxExpertBytes.  The codes are
+// the largest array of every format (scales, zeros and the per-row arrays are smaller).
 wq_status check_product_zp(const wq_weight* w, const char* what) {
   if (is_ccq(w->format) && (w->zp & (w->zp - 1)) != 0)
     return fail(WQ_ERR_UNSUPPORTED, "%s: products need a CCQ zero point of 0 or a power of two", what);
   if (w->k >= (1ll << 30))
     return fail(WQ_ERR_UNSUPPORTED, "%s: products need k below 2^30", what);
   const int64_t row_bytes = row_code_bytes(w);
-  if (w->n * row_bytes >= (1ll << 31))
-    return fail(WQ_ERR_UNSUPPORTED, "%s: one expert's codes must be below 2 GiB", what);
+  if (w->n * row_bytes > kMaxExpertBytes)
+    return fail(WQ_ERR_UNSUPPORTED, "%s: one expert's codes must not exceed %lld bytes", what,
+                (long long)kMaxExpertBytes);
   return WQ_OK;
 }
 
@@ -241,10 +247,11 @@ wq_status wq_quantize_ccq(const float* w, int64_t n, int64_t k, int32_t zp, int3
   if (k > 131072) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_ccq: k = %lld above 131072", (long long)k);
   if (n > 0x7FFFFFFFll) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_ccq: n must be below 2^31");
   if (zp < 0 || zp > 127) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_ccq: zero point must lie in 0..127");
+  if (refine < 0 || refine > 3) return fail(WQ_ERR_ARG, "wq_quantize_ccq: refine is a mask of 1 and 2");
   if (!w || !codes || !qscale || !super_scale || !code_scale || !code_zero)
     return fail(WQ_ERR_ARG, "wq_quantize_ccq: null pointer");
   if (!aligned16(w)) return fail(WQ_ERR_ALIGN, "wq_quantize_ccq: w not 16-byte aligned");
-  return hip_status(wq::launch_ccq_encode(w, n, k, zp, refine != 0, codes, qscale, super_scale,
+  return hip_status(wq::launch_ccq_encode(w, n, k, zp, refine, codes, qscale, super_scale,
                                           code_scale, code_zero, static_cast<hipStream_t>(stream)),
                     "wq_quantize_ccq launch");
 }
@@ -318,8 +325,7 @@ size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t 
 wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t experts,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* ws,
                        size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+  if (ws || ws_bytes) return fail(WQ_ERR_ARG, "wq_moe_route: ws is reserved; pass NULL and 0");
   if (t < 0 || topk <= 0 || experts <= 0) return fail(WQ_ERR_ARG, "wq_moe_route: bad sizes");
   if (experts > kMaxExperts) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_route: at most %d experts", kMaxExperts);
   if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_route: too many pairs");
