@@ -179,6 +179,22 @@ wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t
                      const wq_weight* up, const wq_weight* down, uint16_t* y, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: wq_moe_ffn with its workspace taken from a
+ * library-owned device array of WQ_NOALLOC_SCRATCH_BYTES (32 MiB), which every GPU the library
+ * runs on holds from the first call on it until the process ends.  The caller still passes x,
+ * the routing arrays, the weights and y.  The call itself allocates nothing (no hipMalloc, no
+ * library allocation).  A call whose workspace (wq_moe_workspace_bytes) exceeds the array
+ * returns WQ_ERR_WORKSPACE without launching: at hidden 8192 and inter 3584 that is above 840
+ * (token, slot) pairs, 105 tokens at top-8.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two host threads) race, and must be ordered by
+ * the caller.  Arguments and results are otherwise those of wq_moe_ffn. */
+#define WQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+wq_status wq_moe_ffn_noalloc(const uint16_t* x, int64_t t, int64_t hidden,
+                             const int32_t* topk_ids, const float* topk_weights, int32_t topk,
+                             const wq_weight* gate, const wq_weight* up, const wq_weight* down,
+                             uint16_t* y, void* stream);
+
 /* The stages of wq_moe_ffn, for callers that route elsewhere or time the stages separately
  * (wq_moe_ffn = wq_moe_route + wq_moe_gate_up + wq_moe_down + wq_moe_combine).  The routing
  * arrays are those wq_moe_route produces; npairs = t * topk.  wq_moe_gate_up and wq_moe_down

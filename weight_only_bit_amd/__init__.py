@@ -31,7 +31,8 @@ FMT_INT4, FMT_INT2_AFFINE, FMT_CCQ2, FMT_CCQ432, FMT_CCQ_HYBRID, FMT_INT8 = 1, 2
 # Every symbol include/wq.h declares.
 EXPORTS = ("wq_dequantize", "wq_gemm", "wq_moe_workspace_bytes", "wq_moe_route", "wq_moe_ffn",
            "wq_moe_gate_up", "wq_moe_down", "wq_moe_combine", "wq_pack_int4", "wq_unpack_int4",
-           "wq_packed_size", "wq_status_string", "wq_last_error", "wq_quantize_ccq")
+           "wq_packed_size", "wq_status_string", "wq_last_error", "wq_quantize_ccq",
+           "wq_moe_ffn_noalloc")
 
 
 class WqError(RuntimeError):
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "wq_moe_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
             "wq_moe_route": (i32, [vp, i64, i32, i32, vp, vp, vp, sz, vp]),
             "wq_moe_ffn": (i32, [vp, i64, i64, vp, vp, i32, W, W, W, vp, vp, sz, vp]),
+            "wq_moe_ffn_noalloc": (i32, [vp, i64, i64, vp, vp, i32, W, W, W, vp, vp]),
             "wq_moe_gate_up": (i32, [vp, i64, vp, vp, i32, W, W, vp, vp]),
             "wq_moe_down": (i32, [vp, i64, i32, vp, vp, W, vp, vp]),
             "wq_moe_combine": (i32, [vp, vp, i64, i32, i64, vp, vp]),
@@ -312,6 +314,28 @@ def wq_moe_ffn(x, topk_ids, topk_weights, gate: PackedWeight, up: PackedWeight,
                             ctypes.byref(gate.cstruct()), ctypes.byref(up.cstruct()),
                             ctypes.byref(down.cstruct()), _ptr(y), _ptr(ws), ws.numel(),
                             _stream()), "wq_moe_ffn")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # WQ_NOALLOC_SCRATCH_BYTES
+
+
+def wq_moe_ffn_noalloc(x, topk_ids, topk_weights, gate: PackedWeight, up: PackedWeight,
+                       down: PackedWeight, y):
+    """wq_moe_ffn with the library's own per-GPU scratch array as workspace: the library
+    allocates nothing (the caller passes y).  Calls that overlap on one GPU race."""
+    if x.dim() != 2 or topk_ids.dim() != 2:
+        raise ValueError("wq_moe_ffn_noalloc: x must be [t, hidden] and topk_ids [t, topk]")
+    t, hidden = x.shape
+    topk = topk_ids.shape[1]
+    _need(x, "wq_moe_ffn_noalloc x", "bf16")
+    _need(topk_ids, "wq_moe_ffn_noalloc topk_ids", "i32", shape=(t, topk))
+    _need(topk_weights, "wq_moe_ffn_noalloc topk_weights", "f32", shape=(t, topk))
+    _need(y, "wq_moe_ffn_noalloc y", "bf16", shape=(t, hidden))
+    _check(lib().wq_moe_ffn_noalloc(_ptr(x), t, hidden, _ptr(topk_ids), _ptr(topk_weights), topk,
+                                    ctypes.byref(gate.cstruct()), ctypes.byref(up.cstruct()),
+                                    ctypes.byref(down.cstruct()), _ptr(y), _stream()),
+           "wq_moe_ffn_noalloc")
     return y
 
 

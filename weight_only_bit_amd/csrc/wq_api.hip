@@ -502,33 +502,105 @@ wq_status wq_moe_combine(const float* d, const float* topk_weights, int64_t t, i
                     "wq_moe_combine launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// The body of wq_moe_ffn once a workspace is at hand: validation, then the four stages.
+// `what` names the entry point in error messages; a null ws means the caller's ws was null.
+wq_status moe_ffn_in(const char* what, const uint16_t* x, int64_t t, int64_t hidden,
+                     const int32_t* topk_ids, const float* topk_weights, int32_t topk,
+                     const wq_weight* gate, const wq_weight* up, const wq_weight* down,
+                     uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!gate || !up || !down) return fail(WQ_ERR_ARG, "%s: null descriptor", what);
+  wq_status st = check_moe_weights(gate, up, down, what);
+  if (st != WQ_OK) return st;
+  if (t < 0 || topk <= 0 || hidden <= 0) return fail(WQ_ERR_ARG, "%s: bad sizes", what);
+  if (gate->k != hidden) return fail(WQ_ERR_ARG, "%s: gate/up k must equal hidden", what);
+  if (hidden % 4 != 0) return fail(WQ_ERR_UNSUPPORTED, "%s: hidden must be a multiple of 4", what);
+  if (t == 0) return WQ_OK;
+  if (!x || !topk_ids || !topk_weights || !y || !ws) return fail(WQ_ERR_ARG, "%s: null pointer", what);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws))
+    return fail(WQ_ERR_ALIGN, "%s: x, y and ws must be 16-byte aligned", what);
+  if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "%s: too many pairs", what);
+  const int64_t E = gate->experts, I = gate->n;
+  MoeWs L = moe_layout(ws, t, topk, (int32_t)E, hidden, I);
+  if (ws_bytes < L.bytes)
+    return fail(WQ_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, L.bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = wq::launch_route(topk_ids, t * topk, (int32_t)E, L.offsets, L.sorted, s);
+  if (e != hipSuccess) return hip_status(e, "moe ffn route");
+  e = run_gate_up(x, t, L.offsets, L.sorted, topk, gate, up, L.h, s);
+  if (e != hipSuccess) return hip_status(e, "moe ffn gate/up");
+  e = run_down(L.h, t, topk, L.offsets, L.sorted, down, L.d, s);
+  if (e != hipSuccess) return hip_status(e, "moe ffn down");
+  return hip_status(wq::launch_combine(L.d, topk_weights, t, topk, hidden, y, s), "moe ffn combine");
+}
+
+}  // namespace
+
+extern "C" {
+
 wq_status wq_moe_ffn(const uint16_t* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
                      const float* topk_weights, int32_t topk, const wq_weight* gate,
                      const wq_weight* up, const wq_weight* down, uint16_t* y, void* ws,
                      size_t ws_bytes, void* stream) {
-  if (!gate || !up || !down) return fail(WQ_ERR_ARG, "wq_moe_ffn: null descriptor");
-  wq_status st = check_moe_weights(gate, up, down, "wq_moe_ffn");
-  if (st != WQ_OK) return st;
-  if (t < 0 || topk <= 0 || hidden <= 0) return fail(WQ_ERR_ARG, "wq_moe_ffn: bad sizes");
-  if (gate->k != hidden) return fail(WQ_ERR_ARG, "wq_moe_ffn: gate/up k must equal hidden");
-  if (hidden % 4 != 0) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: hidden must be a multiple of 4");
-  if (t == 0) return WQ_OK;
-  if (!x || !topk_ids || !topk_weights || !y || !ws) return fail(WQ_ERR_ARG, "wq_moe_ffn: null pointer");
-  if (!aligned16(x) || !aligned16(y) || !aligned16(ws))
-    return fail(WQ_ERR_ALIGN, "wq_moe_ffn: x, y and ws must be 16-byte aligned");
-  if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn: too many pairs");
-  const int64_t E = gate->experts, I = gate->n;
-  MoeWs L = moe_layout(ws, t, topk, (int32_t)E, hidden, I);
-  if (ws_bytes < L.bytes)
-    return fail(WQ_ERR_WORKSPACE, "wq_moe_ffn: workspace %zu < %zu bytes", ws_bytes, L.bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = wq::launch_route(topk_ids, t * topk, (int32_t)E, L.offsets, L.sorted, s);
-  if (e != hipSuccess) return hip_status(e, "wq_moe_ffn route");
-  e = run_gate_up(x, t, L.offsets, L.sorted, topk, gate, up, L.h, s);
-  if (e != hipSuccess) return hip_status(e, "wq_moe_ffn gate/up");
-  e = run_down(L.h, t, topk, L.offsets, L.sorted, down, L.d, s);
-  if (e != hipSuccess) return hip_status(e, "wq_moe_ffn down");
-  return hip_status(wq::launch_combine(L.d, topk_weights, t, topk, hidden, y, s), "wq_moe_ffn combine");
+  return moe_ffn_in("wq_moe_ffn", x, t, hidden, topk_ids, topk_weights, topk, gate, up, down, y,
+                    ws, ws_bytes, stream);
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// wq_moe_ffn_noalloc: wq_moe_ffn with its workspace in `scratch`, a file-scope device array of
+// WQ_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its device address is
+// taken once per device with hipGetSymbolAddress (with that device current) and kept in
+// g_scratch_dev; kernels only ever receive that address.  Every call on one GPU shares that
+// GPU's array (calls that overlap on one GPU race).  Nothing in it needs clearing: each call
+// writes every workspace element it reads (offsets, the sorted pairs, h and d of its pairs).
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[WQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the device's first call).
+wq_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "wq_moe_ffn_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(WQ_ERR_UNSUPPORTED, "wq_moe_ffn_noalloc: device id %d is %d or more", dev, kMaxDevices);
+  void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "wq_moe_ffn_noalloc: hipGetSymbolAddress");
+    if (!p) return fail(WQ_ERR_HIP, "wq_moe_ffn_noalloc: no device address for the scratch array");
+    g_scratch_dev[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return WQ_OK;
+}
+
+}  // namespace
+
+extern "C" wq_status wq_moe_ffn_noalloc(const uint16_t* x, int64_t t, int64_t hidden,
+                                        const int32_t* topk_ids, const float* topk_weights,
+                                        int32_t topk, const wq_weight* gate, const wq_weight* up,
+                                        const wq_weight* down, uint16_t* y, void* stream) {
+  if (!gate) return fail(WQ_ERR_ARG, "wq_moe_ffn_noalloc: null descriptor");
+  const size_t need = wq_moe_workspace_bytes(t, topk, (int32_t)gate->experts, hidden, gate->n);
+  if (need > (size_t)WQ_NOALLOC_SCRATCH_BYTES)
+    return fail(WQ_ERR_WORKSPACE,
+                "wq_moe_ffn_noalloc: this call needs %zu bytes of workspace, above the %zu-byte "
+                "scratch array (use wq_moe_ffn with a workspace)",
+                need, (size_t)WQ_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  wq_status st = scratch_address(&ws);
+  if (st != WQ_OK) return st;
+  return moe_ffn_in("wq_moe_ffn_noalloc", x, t, hidden, topk_ids, topk_weights, topk, gate, up,
+                    down, y, ws, (size_t)WQ_NOALLOC_SCRATCH_BYTES, stream);
+}
