@@ -27,15 +27,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_skinny_ccq_gateup_moe_decode.json")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_tiled_ccq_gateup_moe_prefill.json")
 
 
-def kernel_record():
-    """The committed record of the CCQ gate+up kernel (rocprofv3 counter runs, instruction count
-    of its compiled loop), or None when the kernel sources changed since it was taken."""
+def kernel_record(path=TRAFFIC_FILE):
+    """The committed record of a roofline kernel (rocprofv3 counter runs, for the decode kernel
+    also the instruction count of its compiled loop), or None when the kernel sources changed
+    since it was taken."""
     import hashlib
 
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
         h = hashlib.sha256()
         for src in rec["kernel_sources"]:
@@ -46,11 +48,11 @@ def kernel_record():
         return None
 
 
-def measured_traffic():
-    """HBM bytes per launch of the CCQ gate+up kernel from the committed rocprofv3 counter
-    runs (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel sources
-    changed since those counters were taken."""
-    rec = kernel_record()
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch of a roofline kernel from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel sources changed
+    since those counters were taken."""
+    rec = kernel_record(path)
     return int(rec["traffic_bytes_per_launch"]) if rec and "traffic_bytes_per_launch" in rec else None
 
 
@@ -93,6 +95,9 @@ def parse():
     ap.add_argument("--tokens", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=32, help="tokens per sampled layer for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg of the default run")
+    ap.add_argument("--prefill-cpu-tokens", type=int, default=6,
+                    help="tokens of the prefill layer the oracle runs for the prefill CPU baseline")
     ap.add_argument("--wformat", default="ccq", choices=list(WFORMATS),
                     help="2-bit-class format of the MoE layers (moe_stack_decode, moe_prefill): "
                          "ccq = (6,4,3) code cluster, 2.06 bpw (default); ccq432 = (4,3,2), "
@@ -161,6 +166,7 @@ def main():
 
     import synth
     import weight_only_bit_amd as wq
+    from weight_only_bit_amd.stack import MoeStack
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -182,58 +188,50 @@ def main():
             log(f"generated layers 0..{l} ({time.time() - t0:.1f} s)")
     resident = sum(w.nbytes() for lay in layers for w in lay)
     x = torch.from_numpy(synth.acts_bf16((T, H), 500).view(np.int16)).to(dev)
-    routes = []
-    for l in range(L):
-        ids, wts = synth.routing_uniform(T, K, E, 600, l)
-        routes.append((ids, wts, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)))
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    pairs = torch.empty(T * K, dtype=torch.int32, device=dev)
-    h = torch.empty((T * K, I), dtype=torch.bfloat16, device=dev)
-    d = torch.empty((T * K, H), dtype=torch.float32, device=dev)
+    routes_h = [synth.routing_uniform(T, K, E, 600, l) for l in range(L)]
+    routes = [(torch.from_numpy(i).to(dev), torch.from_numpy(w).to(dev)) for i, w in routes_h]
     ys = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    stack = MoeStack(layers, T, K, device=dev)
 
     # Algorithmic bytes: packed weights of the experts each layer routes to.
     per_expert = [[w.nbytes() // E for w in lay] for lay in layers]
-    touched = [len(np.unique(r[0])) for r in routes]
+    touched = [len(np.unique(r[0])) for r in routes_h]
     step_weight_bytes = sum(touched[l] * sum(per_expert[l]) for l in range(L))
     step_act_bytes = L * 2 * T * H * 2  # x read + y written per layer
     ccq_layers = [l for l in range(L) if l >= n4]
 
-    L_ = wq.lib()
-
-    def layer(l, ev=None):
-        g, u, dn = layers[l]
-        ids_d, wts_d = routes[l][2], routes[l][3]
-        st = torch.cuda.current_stream()
-        wq._check(L_.wq_moe_route(wq._ptr(ids_d), T, K, E, wq._ptr(offsets), wq._ptr(pairs), None, 0,
-                                  wq._stream()), "route")
-        if ev is not None:
-            ev[0].record(st)
-        wq.wq_moe_gate_up(x, offsets, pairs, K, g, u, h=h)
-        if ev is not None:
-            ev[1].record(st)
-        wq.wq_moe_down(h, T, K, offsets, pairs, dn, d=d)
-        wq.wq_moe_combine(d, wts_d, y=ys[l])
-
-    def step(evs=None):
-        for l in range(L):
-            layer(l, evs.get(l) if evs is not None else None)
-
-    # ---------------- warmup + timed steps ----------------
-    for _ in range(args.warmup):
-        step()
+    # ---------------- warmup, graph capture, timed steps (graph replays) ----------------
+    for _ in range(max(args.warmup, 1)):
+        stack.step(x, routes, ys)
     torch.cuda.synchronize()
+    stack.capture(x, routes, ys)
+    stack.replay()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record()
+    for s in range(args.steps):
+        stack.replay()
+        marks[s + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [marks[s].elapsed_time(marks[s + 1]) for s in range(args.steps)]
+    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    half = step_ms[args.steps // 2:] if args.steps > 1 else step_ms
+    ms_step_latter = float(np.mean(half))
+
+    # ---------------- eager passes: plain (context) and with events around CCQ gate+up ----
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        stack.step(x, routes, ys)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step_eager = e0.elapsed_time(e1) / args.steps
     evs_all = [{l: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for l in ccq_layers} for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
     for s in range(args.steps):
-        step(evs_all[s])
-    end.record()
+        stack.step(x, routes, ys, events=evs_all[s])
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
     gu_ms = [evs[l][0].elapsed_time(evs[l][1]) for evs in evs_all for l in ccq_layers]
     gu_avg_ms = float(np.mean(gu_ms)) if gu_ms else float("nan")
     # bytes of one CCQ gate+up launch: gate and up of the touched experts + x read + h written
@@ -245,8 +243,9 @@ def main():
 
     value = step_weight_bytes / (ms_step * 1e-3) / 1e9
     tok_s = T / (ms_step * 1e-3)
-    log(f"step {ms_step:.3f} ms, weight stream {value:.1f} GB/s, {tok_s:.1f} tok/s; "
-        f"CCQ gate+up {gu_avg_ms * 1e3:.1f} us avg -> {gu_gbs:.1f} GB/s")
+    log(f"step {ms_step:.3f} ms (graph replay; latter half {ms_step_latter:.3f}, eager {ms_step_eager:.3f}), "
+        f"weight stream {value:.1f} GB/s, {tok_s:.1f} tok/s; CCQ gate+up {gu_avg_ms * 1e3:.1f} us avg "
+        f"-> {gu_gbs:.1f} GB/s")
 
     # ---------------- CPU baseline (oracle on a bounded sample) + spot parity ----------------
     cpu = None
@@ -257,16 +256,18 @@ def main():
         sys.path.insert(0, os.path.join(ROOT, "tests"))
         from wq_testutil import assert_close, torch_bf16_bits
 
+        stack.replay()  # the outputs the parity check reads: one more replay of the step
+        torch.cuda.synchronize()
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         # up to three of the 2-bit-class layers and two INT4 per-channel layers: ~10 s of oracle
         # work on 16 host cores (each layer's touched experts are decoded and multiplied)
         sample_layers = [l for l in (n4, n4 + 1, n4 + 2) if l < L] + [l for l in (0, 1) if l < n4]
         tot_bytes, tot_s, errs = 0, 0.0, []
+        xh = x.cpu().numpy().view(np.uint16)
         for l in sample_layers:
             g, u, dn = (to_host_packed(oracle, w) for w in layers[l])
-            ids, wts = routes[l][0], routes[l][1]
+            ids, wts = routes_h[l]
             toks = np.arange(min(args.cpu_tokens, T), dtype=np.int32)
-            xh = x.cpu().numpy().view(np.uint16)
             t1 = time.perf_counter()
             yref = oracle.moe_ffn(xh, ids, wts, g, u, dn, tokens=toks)
             tot_s += time.perf_counter() - t1
@@ -280,9 +281,9 @@ def main():
                          f"{tot_bytes / 1e9:.3f} GB of packed weights in {tot_s:.1f} s"}
         parity = max(errs)
 
+    prefill = None if args.no_prefill else prefill_leg(args, wq, synth, dev)
     out = {
-        "metric": "weight-stream HBM GB/s (decode M<=32), w2/w4 MoE stack"
-                  + ("" if args.wformat == "ccq" else f" [{WFORMATS[args.wformat][2]}]"),
+        "metric": METRIC + ("" if args.wformat == "ccq" else f" [{WFORMATS[args.wformat][2]}]"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -298,16 +299,26 @@ def main():
                    "ccq_g64_layers": L - n4, "ccq_format": WFORMATS[args.wformat][2], "experts": E, "topk": K, "hidden": H, "inter": I,
                    "tokens": T, "resident_weight_bytes": resident,
                    "step_weight_bytes": step_weight_bytes, "step_activation_bytes": step_act_bytes},
+        "value_note": "the decode half of the metric (weight bytes the step streams / step time); the "
+                      "prefill half is prefill.value (TFLOP/s)",
+        "timing": {"protocol": f"one step ({L} layers) captured in a HIP graph; exactly `steps` replays "
+                               "timed with events around all of them (ms_per_step); per-replay events "
+                               "give the latter half's mean; an eager pass without events for context",
+                   "ms_per_step_latter_half": round(ms_step_latter, 4),
+                   "ms_per_step_eager": round(ms_step_eager, 4)},
         "tokens_per_s": round(tok_s, 2),
         "roofline": {"kernel": f"skinny_kernel {WFORMATS[args.wformat][2]} gate+up (MODE_GATEUP)",
                      "bound": "hbm",
                      "achieved": round(gu_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if args.wformat == "ccq" else None,
                      "avg_launch_us": round(gu_avg_ms * 1e3, 2),
+                     "launch_timing": "HIP events around every CCQ gate+up launch of an eager pass of "
+                                      "`steps` steps after the timed replays, on the launch stream",
                      "algorithmic_bytes_per_launch": int(gu_bytes),
                      "alu": alu_roofline(gu_weights, gu_avg_ms * 1e-3) if args.wformat == "ccq" else None},
         "cpu_baseline": cpu,
         "spot_parity_max_rel_err": parity,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 
@@ -315,29 +326,30 @@ def main():
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 
-def moe_prefill(args):
-    """One CCQ MoE layer at prefill size: 4096 tokens, top-8 of 64 experts, Zipf(1.1)-biased
-    routing.  `value` is unpadded bf16 TFLOP/s of the whole layer (2 * pairs * 3 * hidden * inter
-    per call, routing and combine included); the roofline is the gate+up kernel's, from HIP
-    events around its launches on the stream they run on."""
+METRIC = "weight-stream HBM GB/s (decode M\u226432) + bf16 TFLOP/s (prefill) for w2/w4 GEMM"
+
+
+def prefill_measure(args, wq, synth, dev, cpu_tokens=0):
+    """One MoE layer at prefill size: 4096 tokens, top-8 of 64 experts, Zipf(1.1)-biased routing,
+    weights in the --wformat 2-bit-class format.  Layer TFLOP/s (unpadded: 2 * pairs * 3 *
+    hidden * inter per call, routing and combine included) from events around `steps` calls;
+    the stages one by one from events around each launch, the gate+up stage being the MFMA
+    roofline kernel.  cpu_tokens > 0: the oracle on that many tokens of the same layer (its
+    rate, and the spot parity of those tokens)."""
     import numpy as np
     import torch
 
-    import synth
-    import weight_only_bit_amd as wq
-
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
     E, H, I, K, T = 64, 8192, 3584, 8, 4096
     g, u, dn = make_layer(wq, synth, WFORMATS[args.wformat][0], E, H, I, 2000, 64)
-    x = torch.from_numpy(synth.acts_bf16((T, H), 501).view(np.int16)).to(dev)
+    xh = synth.acts_bf16((T, H), 501)
+    x = torch.from_numpy(xh.view(np.int16)).to(dev)
     ids, wts = synth.routing_zipf(T, K, E, 601)
     ids_d, wts_d = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(wq.wq_moe_workspace_bytes(T, K, E, H, I), dtype=torch.uint8, device=dev)
     P = T * K
     flops = 2.0 * P * 3 * H * I
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 1)):
         wq.wq_moe_ffn(x, ids_d, wts_d, g, u, dn, y=y, ws=ws)
     torch.cuda.synchronize()
     st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -374,27 +386,73 @@ def moe_prefill(args):
     gu_tf = gu_flops / (stage_us["gate_up"] * 1e-6) / 1e12
     dn_tf = 2.0 * P * H * I / (stage_us["down"] * 1e-6) / 1e12
     counts = np.bincount(ids.ravel(), minlength=E)
-    log(f"layer {ms * 1e3:.0f} us ({tf:.1f} TFLOP/s); stages: " +
+    log(f"prefill layer {ms * 1e3:.0f} us ({tf:.1f} TFLOP/s); stages: " +
         ", ".join(f"{k} {v:.0f} us" for k, v in stage_us.items()) +
         f"; gate+up {gu_tf:.1f} TFLOP/s, down {dn_tf:.1f} TFLOP/s")
-    out = {"metric": f"bf16 TFLOP/s (prefill MoE layer, {WFORMATS[args.wformat][2]})",
-           "value": round(tf, 2),
-           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    res = {"value": round(tf, 2), "unit": "TFLOP/s", "ms_per_layer": round(ms, 4),
+           "tokens_per_s": round(T / (ms * 1e-3), 1),
            "config": {"workload": "moe_prefill", "tokens": T, "topk": K, "experts": E,
                       "hidden": H, "inter": I, "routing": "zipf s=1.1",
                       "format": WFORMATS[args.wformat][2],
-                      "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())},
-           "tokens_per_s": round(T / (ms * 1e-3), 1),
+                      "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min()),
+                      "flops_per_layer": flops},
            "stage_us": {k: round(v, 1) for k, v in stage_us.items()},
            "down_tflops": round(dn_tf, 2),
            "roofline": {"kernel": f"tiled_kernel {WFORMATS[args.wformat][2]} gate+up (MODE_GATEUP)",
                         "bound": "mfma",
                         "achieved": round(gu_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "traffic": None, "avg_launch_us": round(stage_us["gate_up"], 1),
+                        "traffic": measured_traffic(PREFILL_TRAFFIC_FILE) if args.wformat == "ccq" else None,
+                        "traffic_note": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB "
+                                        "copy) against 1.276e9 algorithmic bytes (packed gate+up weights "
+                                        "of the 64 experts, x, h)",
+                        "avg_launch_us": round(stage_us["gate_up"], 1),
                         "algorithmic_flops_per_launch": gu_flops}}
+    if cpu_tokens > 0:
+        import oracle
+
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from wq_testutil import assert_close, torch_bf16_bits
+
+        wq.wq_moe_ffn(x, ids_d, wts_d, g, u, dn, y=y, ws=ws)
+        torch.cuda.synchronize()
+        toks = np.linspace(0, T - 1, cpu_tokens).astype(np.int32)
+        host = [to_host_packed(oracle, w) for w in (g, u, dn)]
+        t1 = time.perf_counter()
+        yref = oracle.moe_ffn(xh, ids, wts, *host, tokens=toks)
+        dt = time.perf_counter() - t1
+        err = assert_close(torch_bf16_bits(y)[toks], yref, "bench prefill spot parity")
+        res["cpu_baseline"] = {
+            "value": round(2.0 * len(toks) * K * 3 * H * I / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+            "sample": f"{len(toks)} token(s) of the prefill layer (each with its 8 routed experts "
+                      f"decoded and multiplied), {dt:.1f} s"}
+        res["spot_parity_max_rel_err"] = err
+        log(f"oracle prefill: {len(toks)} tokens in {dt:.1f} s")
+    return res
+
+
+def prefill_leg(args, wq, synth, dev):
+    return prefill_measure(args, wq, synth, dev, 0 if args.no_cpu_baseline else args.prefill_cpu_tokens)
+
+
+def moe_prefill(args):
+    """The prefill layer alone (see prefill_measure); `value` is its TFLOP/s."""
+    import torch
+
+    import synth
+    import weight_only_bit_amd as wq
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    res = prefill_measure(args, wq, synth, dev, 0 if args.no_cpu_baseline else args.prefill_cpu_tokens)
+    out = {"metric": f"bf16 TFLOP/s (prefill MoE layer, {WFORMATS[args.wformat][2]})",
+           "value": res["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": res["ms_per_layer"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": res["config"], "tokens_per_s": res["tokens_per_s"], "stage_us": res["stage_us"],
+           "down_tflops": res["down_tflops"], "roofline": res["roofline"],
+           "cpu_baseline": res.get("cpu_baseline")}
     print(json.dumps(out), flush=True)
 
 
