@@ -340,6 +340,10 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
+// SiLU(v) = v / (1 + e^-v) with the hardware exponential and reciprocal (about one ulp each;
+// h is rounded to bf16 right after, 2^-9 relative).
+__device__ __forceinline__ float silu_f32(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
 
 }  // namespace wq

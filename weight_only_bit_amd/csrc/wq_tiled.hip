@@ -605,32 +605,58 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   if (g + 2 < steps) iter(g + 2, std::integral_constant<int, 2>{});
   __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the wave exits
 
-  // ---- epilogue: lane holds D[8 (r/4) + 4 kh + r % 4][l32] of each 32 x 32 tile ----
+  // ---- epilogue: lane holds D[m][wrow[j]] for m = 32 i + 8 q + 4 kh + t, r = 4 q + t, of each
+  // 32 x 32 tile i.  Row m's store address is a per-lane base plus m x the row stride, a
+  // uniform (scalar) product; down rows go to their pair's row of d, the pair ids of the tile's
+  // rows staged once in LDS (activation stage 0: every wave's copies have landed and its reads
+  // returned once all waves pass the barrier below), four consecutive rows per read. ----
+  const bool full_rows = rows == 32 * MT;
+  if constexpr (MODE == MODE_DOWN) {
+    int32_t* s_pair = reinterpret_cast<int32_t*>(a_stage<0>());
+    __syncthreads();
+    for (int m = tid; m < 32 * MT; m += NTHREADS)
+      s_pair[m] = args.sorted_pairs[row0 + (m < rows ? m : 0)];
+    __syncthreads();
+    float* d = reinterpret_cast<float*>(args.out);
+    const int64_t stride = args.out_stride;
+    const bool in0 = wrow[0] < N, in1 = wrow[1] < N;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 32 * i + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (m >= rows) continue;
-      const int64_t grow = row0 + m;
-      if constexpr (MODE == MODE_GATEUP) {
-        const int64_t n = wrow[0];
-        if (n >= N) continue;
-        uint16_t* h = reinterpret_cast<uint16_t*>(args.out);
-        h[grow * args.out_stride + n] =
-            (uint16_t)f32_to_bf16_bits(silu_f32(acc[i][0][r]) * acc[i][1][r]);
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        const int m0 = 32 * i + 8 * q + 4 * kh;
+        const int4 pr = *reinterpret_cast<const int4*>(s_pair + m0);
+        const int32_t pid[4] = {pr.x, pr.y, pr.z, pr.w};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t n = wrow[j];
-          if (n >= N) continue;
-          if constexpr (MODE == MODE_DENSE) {
-            uint16_t* y = reinterpret_cast<uint16_t*>(args.out);
-            y[grow * args.out_stride + n] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+        for (int t = 0; t < 4; ++t) {
+          if (!full_rows && m0 + t >= rows) continue;
+          float* drow = d + (int64_t)pid[t] * stride;
+          if (in0) drow[wrow[0]] = acc[i][0][4 * q + t];
+          if (in1) drow[wrow[1]] = acc[i][1][4 * q + t];
+        }
+      }
+    }
+  } else {
+    uint16_t* out = reinterpret_cast<uint16_t*>(args.out);
+    const int64_t stride = args.out_stride;
+    uint16_t* base = out + (row0 + 4 * kh) * stride;
+#pragma unroll
+    for (int j = 0; j < (MODE == MODE_GATEUP ? 1 : 2); ++j) {
+      const int64_t n = wrow[j];
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mc = 32 * i + 8 * (r >> 2) + (r & 3);  // m - 4 kh: the uniform part of the row
+          if (!full_rows && mc + 4 * kh >= rows) continue;
+          float v;
+          if constexpr (MODE == MODE_GATEUP) {
+            v = silu_f32(acc[i][0][r]) * acc[i][1][r];
           } else {
-            float* d = reinterpret_cast<float*>(args.out);
-            d[(int64_t)args.sorted_pairs[grow] * args.out_stride + n] = acc[i][j][r];
+            v = acc[i][j][r];
           }
+          base[(int64_t)mc * stride + n] = (uint16_t)f32_to_bf16_bits(v);
         }
       }
     }
