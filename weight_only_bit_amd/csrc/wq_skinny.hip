@@ -362,6 +362,18 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
 #pragma unroll
       for (int j = 0; j < LPW; ++j) srow[j] = args.a + (int64_t)sidx[j] * args.a_stride;
     }
+    // down: the pair ids of the lane's output rows, loaded before the chunk loop so that the
+    // epilogue's stores wait for no memory round trip
+    int32_t pid[MT][4];
+    if constexpr (MODE == MODE_DOWN) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = t * 16 + 4 * kb + i;
+          pid[t][i] = args.sorted_pairs[m_base + ms + (m < rows_here ? m : 0)];
+        }
+    }
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int seg = (wave * LPW + j) % SEGS;
@@ -488,8 +500,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs args) {
                 (uint16_t)f32_to_bf16_bits(silu_f32(acc[t][i]) * up[t][i]);
           } else {
             float* d = reinterpret_cast<float*>(args.out);
-            const int64_t pair = args.sorted_pairs[r];
-            d[pair * args.out_stride + nrow] = acc[t][i];
+            d[(int64_t)pid[t][i] * args.out_stride + nrow] = acc[t][i];
           }
         }
       }
