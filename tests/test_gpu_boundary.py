@@ -101,3 +101,26 @@ def test_products_at_the_scale_limit(wq, name, fmt, group, factor):
         y = wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), d)
         torch.cuda.synchronize()
         assert_close(torch_bf16_bits(y), oracle.gemm(x, p), f"scale limit {name} m={m}")
+
+
+def test_gemm_with_activations_of_4gib_or_more(wq):
+    """The tiled kernels address an activation row by a 32-bit offset from the array's base; an
+    activation array of 4 GiB or more runs the decode-streaming kernels instead.  x here is
+    32768 x 65536 bf16 = 4 GiB; sampled rows (first, last, and across the array) against the
+    oracle."""
+    import torch
+
+    m, k, n = 32768, 65536, 64
+    _say(f"gemm with a 4 GiB activation array ({m} x {k})")
+    p = oracle.quantize(synth.weights_f32((n, k), 74, 1), oracle.CCQ)
+    x = torch.empty((m, k), dtype=torch.bfloat16, device="cuda")
+    rows = np.array([0, 1, 12345, m // 2, m - 2, m - 1])
+    xs = synth.acts_bf16((len(rows), k), 74, 2)
+    x.zero_()
+    x[torch.from_numpy(rows).cuda()] = torch.from_numpy(xs.view(np.int16)).cuda().view(torch.bfloat16)
+    y = wq.wq_gemm(x, to_device(p))
+    torch.cuda.synchronize()
+    got = torch_bf16_bits(y)[rows]
+    del x, y
+    torch.cuda.empty_cache()
+    assert_close(got, oracle.gemm(xs, p), "gemm 4 GiB activations")
