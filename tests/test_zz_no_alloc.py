@@ -84,3 +84,49 @@ def test_noalloc_small_layer_against_oracle(wq):
                              torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda(), mats)
         assert np.array_equal(got, ref), (call, T)
         assert_close(got, oracle.moe_ffn(xh, ids, wts, *host), f"noalloc small layer call {call}")
+
+
+def test_noalloc_captured_in_a_graph(wq):
+    """The callers this entry point is for include code under HIP graph capture: a captured
+    call replays the eager result bit for bit, also after eager calls with other inputs have
+    overwritten the scratch array in between (nothing in it needs clearing)."""
+    import torch
+
+    E, H, I, K = 8, 1024, 512, 2
+    host = [oracle.quantize(synth.weights_f32(s, 9120, j), oracle.CCQ)
+            for j, s in enumerate(((E, I, H), (E, I, H), (E, H, I)))]
+    mats = [to_device(p) for p in host]
+
+    def inputs(T, seed):
+        xh = synth.acts_bf16((T, H), 9121, seed)
+        ids, wts = synth.routing_uniform(T, K, E, 9122, seed)
+        return (xh, ids, wts, torch.from_numpy(xh.view(np.int16)).cuda(),
+                torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda())
+
+    xh, ids, wts, x, ids_d, wts_d = inputs(12, 1)
+    y = torch.empty((12, H), dtype=torch.bfloat16, device="cuda")
+    wq.wq_moe_ffn_noalloc(x, ids_d, wts_d, *mats, y=y)  # warm-up: one-time set-up outside capture
+    torch.cuda.synchronize()
+    eager = torch_bf16_bits(y).copy()
+    assert_close(eager, oracle.moe_ffn(xh, ids, wts, *host), "noalloc eager before capture")
+    _say("noalloc: graph capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wq.wq_moe_ffn_noalloc(x, ids_d, wts_d, *mats, y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.wq_moe_ffn_noalloc(x, ids_d, wts_d, *mats, y=y)
+    other = inputs(20, 2)
+    y2 = torch.empty((20, H), dtype=torch.bfloat16, device="cuda")
+    for rep in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(torch_bf16_bits(y), eager), rep
+        wq.wq_moe_ffn_noalloc(other[3], other[4], other[5], *mats, y=y2)  # overwrites the scratch
+        torch.cuda.synchronize()
+    assert_close(torch_bf16_bits(y2), oracle.moe_ffn(other[0], other[1], other[2], *host),
+                 "noalloc eager between replays")
