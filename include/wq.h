@@ -251,9 +251,12 @@ wq_status wq_pack_int4(const int32_t* codes, int64_t n, uint8_t* out);
 wq_status wq_unpack_int4(const uint8_t* data, int64_t n, int32_t* out);
 int64_t wq_packed_size(int64_t n_codes, int32_t bits);
 
-/* Name of a status code, and the detail of the calling thread's last failure. */
+/* Name of a status code, and the detail of the calling thread's last failure (the text stays
+ * valid until that thread's next failing call; wq_last_error_detail is the same call under a
+ * second name). */
 const char* wq_status_string(int32_t status);
 const char* wq_last_error(void);
+const char* wq_last_error_detail(void);
 
 #ifdef __cplusplus
 }

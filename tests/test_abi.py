@@ -169,6 +169,16 @@ def test_route_workspace_is_reserved(wq):
     assert b"reserved" in L.wq_last_error()
 
 
+def test_last_error_detail_is_the_last_failure_under_both_names(wq):
+    L = wq.lib()
+    assert L.wq_pack_int4((ctypes.c_int32 * 2)(3, 9), 2, (ctypes.c_uint8 * 1)()) == -4
+    assert b"outside -8..7" in L.wq_last_error_detail()
+    assert L.wq_last_error_detail() == L.wq_last_error()
+    assert L.wq_moe_route(None, 1, 1, 1, None, None, None, 0, None) == -1
+    assert L.wq_last_error_detail() == L.wq_last_error() != b""
+    assert b"outside -8..7" not in L.wq_last_error_detail()
+
+
 def test_products_reject_experts_beyond_the_32bit_buffer_range(wq):
     """One expert's codes are addressed through 32-bit buffer resources whose range the
     kernels cap at 0x7FFFFFF0 bytes (plus up to 6 bytes of dword alignment for the (4,3,2) and

@@ -31,7 +31,7 @@ FMT_INT4, FMT_INT2_AFFINE, FMT_CCQ2, FMT_CCQ432, FMT_CCQ_HYBRID, FMT_INT8 = 1, 2
 # Every symbol include/wq.h declares.
 EXPORTS = ("wq_dequantize", "wq_gemm", "wq_moe_workspace_bytes", "wq_moe_route", "wq_moe_ffn",
            "wq_moe_gate_up", "wq_moe_down", "wq_moe_combine", "wq_pack_int4", "wq_unpack_int4",
-           "wq_packed_size", "wq_status_string", "wq_last_error", "wq_quantize_ccq",
+           "wq_packed_size", "wq_status_string", "wq_last_error", "wq_last_error_detail", "wq_quantize_ccq",
            "wq_moe_ffn_noalloc")
 
 
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "wq_packed_size": (i64, [i64, i32]),
             "wq_status_string": (ctypes.c_char_p, [i32]),
             "wq_last_error": (ctypes.c_char_p, []),
+            "wq_last_error_detail": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)

@@ -201,6 +201,8 @@ const char* wq_status_string(int32_t st) {
 
 const char* wq_last_error(void) { return g_last_error.c_str(); }
 
+const char* wq_last_error_detail(void) { return g_last_error.c_str(); }
+
 wq_status wq_pack_int4(const int32_t* codes, int64_t n, uint8_t* out) {
   if (n < 0 || (n > 0 && (!codes || !out))) return fail(WQ_ERR_ARG, "wq_pack_int4: bad arguments");
   for (int64_t i = 0; i < n; ++i)
