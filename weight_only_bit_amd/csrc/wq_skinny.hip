@@ -2,7 +2,7 @@
 //
 // Every packed weight byte is read from HBM once per pass and decoded in registers straight
 // into MFMA B-operand fragments (exact bf16 weights, see wq_device.hpp); nothing decoded goes
-// through LDS or memory.  The decode is VALU work (about 4.5 instructions per CCQ weight), so
+// through LDS or memory.  The decode is VALU work (about 2.8 instructions per CCQ weight), so
 // the layout aims at keeping every SIMD's VALU busy:
 //
 //   * one workgroup = 4 waves of 64; each wave decodes ONE weight matrix for a 16-row tile of
