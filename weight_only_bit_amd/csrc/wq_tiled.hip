@@ -504,18 +504,15 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
     read_codes(cc, cstc);
     decode_rows(cc, g, dst);
   };
-  // Memory instructions issued per iteration: packed data, then the 8 activation copies.
-  constexpr int VMEM_PER_ITER = Ring::VMEM + MT;
   constexpr int CD = Ring::DEPTH;
 
-  // ---- prologue: steps 0..2 of the activations and 0..AHEAD-1 of the packed data in flight,
-  // step 0 decoded and visible ----
+  // ---- prologue: steps 0 and 1 of the activations and 0..AHEAD-1 of the packed data in
+  // flight, step 0 decoded and visible ----
   copy_codes(0, std::integral_constant<int, 0>{});
   copy_a(0, std::integral_constant<int, 0>{});
   copy_codes(clamp_step(1), std::integral_constant<int, 1 % CD>{});
   copy_a(clamp_step(1), std::integral_constant<int, 1>{});
   if constexpr (Ring::AHEAD > 2) copy_codes(clamp_step(2), std::integral_constant<int, 2 % CD>{});
-  copy_a(clamp_step(2), std::integral_constant<int, 2>{});
   __builtin_amdgcn_s_waitcnt(0);  // everything issued so far
   __syncthreads();
   decode_step(0, std::integral_constant<int, 0>{}, Bw[0]);
@@ -523,22 +520,30 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   read_a(X, 0, std::integral_constant<int, 0>{});
 
   // ---- main loop: iteration g multiplies step g (LDS stage g % 4, B parity g % 2) ----
-  //   wait for step g + 1's copies; issue the packed data of step g + AHEAD; then slices 0..2
-  //   (slice 0 was read last iteration), the next slices' reads, the decode of step g + 1 and
-  //   the activation copies of step g + 3 (one after each of the first MFMAs); barrier; read
-  //   slice 0 of step g + 1 under slice 3 of step g.
-  // The activation copies go to the stage of step g - 1, whose last reads every wave made, and
-  // saw return, before the previous iteration's barrier, and the packed data to this wave's own stage of
-  // step g + AHEAD - CD, read at the start of an earlier iteration: neither needs this
-  // iteration's barrier, so both are issued before it, in the shadow of the MFMAs.
+  //   wait for step g + 1's packed data; issue the packed data of step g + AHEAD; on even g the
+  //   activation copies of steps g + 2 and g + 3 (two after each of the first MFMAs); slices
+  //   0..2 (slice 0 was read last iteration), the next slices' reads and the decode of step
+  //   g + 1; on odd g, once this wave's copies of steps g + 1 and g + 2 have landed, the
+  //   barrier; read slice 0 of step g + 1 under slice 3 of step g.
+  // The barrier comes every second step.  Even iteration g copies into the stages of steps
+  // g - 2 and g - 1, whose last reads every wave made, and saw return, before the barrier that
+  // ended iteration g - 1; a stage's copies are known landed in every wave at the barrier after
+  // the odd iteration that follows them, before any wave reads that stage (step g + 1 of an
+  // even g was copied two iterations earlier).  The packed data goes to this wave's own stage
+  // of step g + AHEAD - CD, read at the start of an earlier iteration.
   auto iter = [&](int64_t g, auto stc) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
     constexpr int PB = ST & 1;
-    // This wave's copies of step g + 1 have landed once at most the previous iteration's
-    // memory instructions are outstanding -- or, when the packed data runs only two steps
-    // ahead, its activation copies (issued after its packed data: the sched_barrier below
-    // keeps that order).
-    WQ_WAIT_VMCNT(Ring::AHEAD >= 3 ? VMEM_PER_ITER : MT);
+    constexpr bool EVEN = PB == 0;
+    // This wave's packed data of step g + 1 has landed once at most the memory instructions
+    // issued after it are outstanding: on odd g the last iteration's (its packed data and 2 MT
+    // activation copies; with the packed data only two steps ahead, just the copies); on even g
+    // the wait before the last barrier covered it, unless it was issued in that odd iteration
+    // itself (two steps ahead).
+    if constexpr (!EVEN)
+      WQ_WAIT_VMCNT(Ring::AHEAD >= 3 ? Ring::VMEM + 2 * MT : 2 * MT);
+    else if constexpr (Ring::AHEAD < 3)
+      WQ_WAIT_VMCNT(0);
     // slice 0's fragments (read under the previous iteration's last MFMAs) are complete; saying
     // so here spares the first MFMA a wait that would also cover the reads issued below
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
@@ -546,7 +551,10 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
     read_codes(cc, std::integral_constant<int, (ST + 1) % CD>{});
     copy_codes(clamp_step(g + Ring::AHEAD), std::integral_constant<int, (ST + Ring::AHEAD) % CD>{});
     __builtin_amdgcn_sched_barrier(0);
-    copy_a(clamp_step(g + 3), std::integral_constant<int, (ST + 3) & 3>{});
+    if constexpr (EVEN) {
+      copy_a(clamp_step(g + 2), std::integral_constant<int, (ST + 2) & 3>{});
+      copy_a(clamp_step(g + 3), std::integral_constant<int, (ST + 3) & 3>{});
+    }
     read_a(Y, 1, stc);
     mma(X, Bw[PB], 0);
     read_a(X, 2, stc);
@@ -561,7 +569,7 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if constexpr (EVEN) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
@@ -582,10 +590,15 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 40 / MT, 0);
     }
-    // every LDS read of this wave has returned before it arrives: a stage read before this
-    // barrier may be overwritten by any wave's copies in the next iteration
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
+    if constexpr (!EVEN) {
+      // this wave's copies of steps g + 1 and g + 2 have landed once at most this iteration's
+      // packed data is outstanding, and every LDS read of this wave has returned before it
+      // arrives: a stage read before this barrier may be overwritten by any wave's copies in
+      // the next iteration
+      WQ_WAIT_VMCNT(Ring::VMEM);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+    }
     __builtin_amdgcn_sched_barrier(0);
     read_a(X, 0, std::integral_constant<int, (ST + 1) & 3>{});
     mma(Y, Bw[PB], 3);
