@@ -241,7 +241,8 @@ def test_tiled_gemm_repeatable_short_k(wq, name):
     import torch
 
     fmt, group = _fmt_group(name)
-    for k in (64, 128, 192):
+    # 1, 2, 3 steps (tails only), 4 (one unrolled loop pass), 5 and 7 (a pass plus odd tails)
+    for k in (64, 128, 192, 256, 320, 448):
         n, m = 320, 64
         p = _quant(fmt, (n, k), (21, fmt, group, k), group=group)
         x = synth.acts_bf16((m, k), 22, k)
