@@ -12,10 +12,12 @@ names the passage of the pages it follows:
 * [WINT2] FastDeploy "WINT2 Quantization"
 * [E6.4]  coursefy lesson E6.4 "GPTQ and AWQ"
 
-Parity status: every function is pinned by tests in ``tests/test_oracle_*.py`` except the
-first stage of the code-cluster decode (``ccq_expand``), which the pages give no numeric
-example for: it is pinned only by invariants and an exact-rational re-statement
-("parity unpinned" by the pages).
+Parity status: every function is pinned by tests in ``tests/test_oracle_*.py``.  The first
+stage of the code-cluster decode (``ccq_expand``) has no numeric example in the pages; it is
+pinned by the code cluster's round trip (Eq. 1 of [CCQ]: on encoder rows with alpha != 1 every
+expanded code lies within alpha / 2 + 1/2 of the code it stands for, which fixes the direction
+C' * alpha + beta and the roles of alpha and beta) and by invariants (identity, clamps,
+monotonicity).
 """
 from __future__ import annotations
 
