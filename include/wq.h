@@ -147,18 +147,26 @@ wq_status wq_gemm(const uint16_t* x, int64_t m, const wq_weight* w, uint16_t* y,
 
 /* Bytes of device workspace wq_moe_ffn needs for t tokens, top-k routing over `experts`
  * experts, hidden size `hidden` and expert intermediate size `inter` (expert offsets, the
- * sorted pair list, h and d of the stages below).  0 for invalid sizes. */
+ * sorted pair list, h and d of the stages below, and above 4096 pairs the routing table of
+ * wq_moe_route_workspace_bytes).  0 for invalid sizes. */
 size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t hidden,
                               int64_t inter);
+
+/* Bytes of device workspace that lets wq_moe_route sort t*topk pairs in chunks, one
+ * workgroup per chunk (a per-chunk table of counts per expert); 0 when the sort takes no
+ * workspace (at most 4096 pairs) or for invalid sizes. */
+size_t wq_moe_route_workspace_bytes(int64_t t, int32_t topk, int32_t experts);
 
 /* Group the (token, slot) pairs p = t*topk + j by expert (sort by expert id, stable in p):
  * expert_offsets[e] = number of pairs routed to experts < e (expert_offsets[experts] =
  * t*topk); sorted_pairs[expert_offsets[e] ...] lists expert e's pairs in increasing p.
  * topk_ids int32 [t][topk] must lie in [0, experts); the device drops a pair whose id lies
  * outside (it lands in no expert's list and nothing is written out of bounds), and the
- * outputs of its token are then unspecified.  ws and ws_bytes are reserved (routing needs no
- * workspace): pass NULL and 0, anything else returns WQ_ERR_ARG.  At most 512 experts and
- * 2^30 pairs. */
+ * outputs of its token are then unspecified.  ws: NULL (ws_bytes 0) sorts in one workgroup;
+ * device memory of at least wq_moe_route_workspace_bytes bytes (caller-owned, nothing in it
+ * needs to be initialized) lets a long array be sorted in chunks over many workgroups, with the
+ * same result.  A non-NULL ws smaller than that returns WQ_ERR_WORKSPACE, a NULL ws with a
+ * non-zero size WQ_ERR_ARG.  At most 512 experts and 2^30 pairs. */
 wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t experts,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* ws,
                        size_t ws_bytes, void* stream);

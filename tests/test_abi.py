@@ -160,13 +160,27 @@ def test_quantize_ccq_argument_checks(wq):
         assert L.wq_quantize_ccq(p[0], 4, 256, 32, bad, *p[1:], None) == -1
 
 
-def test_route_workspace_is_reserved(wq):
+def test_route_workspace_sizes_and_checks(wq):
     L = wq.lib()
+    # no table at most 4096 pairs; above, chunks of max(2048, ceil(pairs / 512)) pairs, one
+    # int32 per chunk and expert
+    assert L.wq_moe_route_workspace_bytes(32, 8, 64) == 0
+    assert L.wq_moe_route_workspace_bytes(512, 8, 64) == 0
+    assert L.wq_moe_route_workspace_bytes(513, 8, 64) == 3 * 64 * 4
+    assert L.wq_moe_route_workspace_bytes(4096, 8, 64) == 16 * 64 * 4
+    assert L.wq_moe_route_workspace_bytes(1 << 27, 8, 512) == 512 * 512 * 4
+    for bad in ((-1, 8, 64), (4, 0, 64), (4, 8, 0), (4, 8, 513), ((1 << 27) + 1, 8, 64)):
+        assert L.wq_moe_route_workspace_bytes(*bad) == 0, bad
+    # the FFN workspace holds the table above 4096 pairs
+    base = L.wq_moe_workspace_bytes(4096, 8, 64, 256, 128)
+    assert base >= 16 * 64 * 4 + 4096 * 8 * (4 + 2 * 128 + 4 * 256)
     ids = ctypes.c_void_p(0x50000)
     off, pairs = ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000)
-    assert L.wq_moe_route(ids, 4, 2, 8, off, pairs, ctypes.c_void_p(0x80000), 0, None) == -1
     assert L.wq_moe_route(ids, 4, 2, 8, off, pairs, None, 256, None) == -1
-    assert b"reserved" in L.wq_last_error()
+    assert b"without a workspace" in L.wq_last_error()
+    need = L.wq_moe_route_workspace_bytes(4096, 8, 64)
+    assert L.wq_moe_route(ids, 4096, 8, 64, off, pairs, ctypes.c_void_p(0x80000), need - 4, None) == -5
+    assert L.wq_moe_route(ids, 4096, 8, 64, off, pairs, ctypes.c_void_p(0x80008), need, None) == -3
 
 
 def test_last_error_detail_is_the_last_failure_under_both_names(wq):

@@ -304,25 +304,33 @@ def test_gemm_alg2_random_words_bit_exact(wq, name):
                                                  (33, 4, 300, "uniform"), (50, 1, 1, "uniform"),
                                                  (20, 8, 512, "uniform"), (1000, 6, 16, "zipf"),
                                                  (0, 8, 64, "uniform"), (128, 8, 64, "zipf"),
-                                                 (129, 8, 64, "zipf")])
+                                                 (129, 8, 64, "zipf"),
+                                                 # above 4096 pairs: sorted in chunks of >= 2048
+                                                 (513, 8, 64, "uniform"), (700, 8, 300, "zipf"),
+                                                 (3000, 2, 1, "uniform"), (12501, 8, 512, "uniform"),
+                                                 (131072, 8, 64, "zipf")])
 def test_route_exact(wq, t, topk, experts, kind):
+    # both the one-workgroup sort and, for long arrays, the chunked one (its workspace from
+    # wq_moe_route_workspace_bytes) against the oracle's stable sort
     import torch
 
     _say(f"route t={t} topk={topk} E={experts} {kind}")
     gen = synth.routing_zipf if kind == "zipf" else synth.routing_uniform
     ids, _ = gen(t, topk, experts, 8, t)
     off_ref, pairs_ref = oracle.moe_route(ids, experts)
-    off, pairs = wq.wq_moe_route(torch.from_numpy(ids).cuda(), experts)
-    assert np.array_equal(off.cpu().numpy(), off_ref)
-    assert np.array_equal(pairs.cpu().numpy(), pairs_ref)
+    ids_d = torch.from_numpy(ids).cuda()
+    for chunked in (True, False):
+        off, pairs = wq.wq_moe_route(ids_d, experts, chunked=chunked)
+        assert np.array_equal(off.cpu().numpy(), off_ref), chunked
+        assert np.array_equal(pairs.cpu().numpy(), pairs_ref), chunked
 
 
-@pytest.mark.parametrize("t,experts", [(40, 64), (300, 16)])
+@pytest.mark.parametrize("t,experts", [(40, 64), (300, 16), (1000, 64)])
 def test_route_drops_ids_out_of_range(wq, t, experts):
     # Ids outside [0, E) are dropped: the offsets count the valid pairs only and the first
     # offsets[E] slots hold the valid pairs grouped by expert in increasing pair order (checked
     # against a direct count, since the oracle refuses such tables).  40 x 8 pairs take the
-    # few-pairs kernel, 300 x 8 the counter-row kernel.
+    # few-pairs kernel, 300 x 8 the counter-row kernel, 1000 x 8 the chunked sort.
     import torch
 
     ids, _ = synth.routing_uniform(t, 8, experts, 9, t)

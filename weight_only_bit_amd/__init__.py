@@ -29,7 +29,8 @@ WQ_ERR_HIP = -6
 FMT_INT4, FMT_INT2_AFFINE, FMT_CCQ2, FMT_CCQ432, FMT_CCQ_HYBRID, FMT_INT8 = 1, 2, 3, 4, 5, 6
 
 # Every symbol include/wq.h declares.
-EXPORTS = ("wq_dequantize", "wq_gemm", "wq_moe_workspace_bytes", "wq_moe_route", "wq_moe_ffn",
+EXPORTS = ("wq_dequantize", "wq_gemm", "wq_moe_workspace_bytes", "wq_moe_route_workspace_bytes",
+           "wq_moe_route", "wq_moe_ffn",
            "wq_moe_gate_up", "wq_moe_down", "wq_moe_combine", "wq_pack_int4", "wq_unpack_int4",
            "wq_packed_size", "wq_status_string", "wq_last_error", "wq_last_error_detail", "wq_quantize_ccq",
            "wq_moe_ffn_noalloc")
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "wq_dequantize": (i32, [W, vp, vp]),
             "wq_gemm": (i32, [vp, i64, W, vp, vp]),
             "wq_moe_workspace_bytes": (sz, [i64, i32, i32, i64, i64]),
+            "wq_moe_route_workspace_bytes": (sz, [i64, i32, i32]),
             "wq_moe_route": (i32, [vp, i64, i32, i32, vp, vp, vp, sz, vp]),
             "wq_moe_ffn": (i32, [vp, i64, i64, vp, vp, i32, W, W, W, vp, vp, sz, vp]),
             "wq_moe_ffn_noalloc": (i32, [vp, i64, i64, vp, vp, i32, W, W, W, vp, vp]),
@@ -277,8 +279,13 @@ def wq_moe_workspace_bytes(t: int, topk: int, experts: int, hidden: int, inter: 
     return int(lib().wq_moe_workspace_bytes(t, topk, experts, hidden, inter))
 
 
-def wq_moe_route(topk_ids, experts: int):
-    """(expert_offsets int32 [E+1], sorted_pairs int32 [t*topk]) on the device."""
+def wq_moe_route_workspace_bytes(t: int, topk: int, experts: int) -> int:
+    return int(lib().wq_moe_route_workspace_bytes(t, topk, experts))
+
+
+def wq_moe_route(topk_ids, experts: int, chunked: bool = True):
+    """(expert_offsets int32 [E+1], sorted_pairs int32 [t*topk]) on the device.  chunked: sort a
+    long array over many workgroups with a workspace (same result); False sorts in one."""
     import torch
 
     if topk_ids.dim() != 2:
@@ -287,8 +294,11 @@ def wq_moe_route(topk_ids, experts: int):
     _need(topk_ids, "wq_moe_route topk_ids", "i32")
     off = torch.empty(experts + 1, dtype=torch.int32, device=topk_ids.device)
     pairs = torch.empty(t * topk, dtype=torch.int32, device=topk_ids.device)
-    _check(lib().wq_moe_route(_ptr(topk_ids), t, topk, experts, _ptr(off), _ptr(pairs), None, 0,
-                              _stream()), "wq_moe_route")
+    nws = wq_moe_route_workspace_bytes(t, topk, experts) if chunked else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=topk_ids.device) if nws else None
+    _check(lib().wq_moe_route(_ptr(topk_ids), t, topk, experts, _ptr(off), _ptr(pairs),
+                              _ptr(ws) if ws is not None else None, nws, _stream()),
+           "wq_moe_route")
     return off, pairs
 
 

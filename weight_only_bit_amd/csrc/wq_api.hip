@@ -152,6 +152,7 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 struct MoeWs {
   int32_t* offsets;
   int32_t* sorted;
+  int32_t* route_table;  // null when the routing sort takes no table
   uint16_t* h;
   float* d;
   size_t bytes;
@@ -166,6 +167,9 @@ MoeWs moe_layout(void* ws, int64_t t, int32_t topk, int32_t experts, int64_t hid
   off = align_up(off + sizeof(int32_t) * ((size_t)experts + 1));
   L.sorted = reinterpret_cast<int32_t*>(b + off);
   off = align_up(off + sizeof(int32_t) * pairs);
+  const int64_t table = wq::route_table_entries((int64_t)pairs, experts);
+  L.route_table = table > 0 ? reinterpret_cast<int32_t*>(b + off) : nullptr;
+  off = align_up(off + sizeof(int32_t) * (size_t)table);
   L.h = reinterpret_cast<uint16_t*>(b + off);
   off = align_up(off + sizeof(uint16_t) * pairs * (size_t)inter);
   L.d = reinterpret_cast<float*>(b + off);
@@ -324,16 +328,27 @@ size_t wq_moe_workspace_bytes(int64_t t, int32_t topk, int32_t experts, int64_t 
   return moe_layout(nullptr, t, topk, experts, hidden, inter).bytes;
 }
 
+size_t wq_moe_route_workspace_bytes(int64_t t, int32_t topk, int32_t experts) {
+  if (t < 0 || topk <= 0 || experts <= 0 || experts > kMaxExperts || (int64_t)t * topk > (1ll << 30))
+    return 0;
+  return sizeof(int32_t) * (size_t)wq::route_table_entries(t * topk, experts);
+}
+
 wq_status wq_moe_route(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t experts,
                        int32_t* expert_offsets, int32_t* sorted_pairs, void* ws,
                        size_t ws_bytes, void* stream) {
-  if (ws || ws_bytes) return fail(WQ_ERR_ARG, "wq_moe_route: ws is reserved; pass NULL and 0");
+  if (!ws && ws_bytes) return fail(WQ_ERR_ARG, "wq_moe_route: a workspace size without a workspace");
   if (t < 0 || topk <= 0 || experts <= 0) return fail(WQ_ERR_ARG, "wq_moe_route: bad sizes");
   if (experts > kMaxExperts) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_route: at most %d experts", kMaxExperts);
   if ((int64_t)t * topk > (1ll << 30)) return fail(WQ_ERR_UNSUPPORTED, "wq_moe_route: too many pairs");
+  const size_t need = wq_moe_route_workspace_bytes(t, topk, experts);
+  if (ws && ws_bytes < need)
+    return fail(WQ_ERR_WORKSPACE, "wq_moe_route: workspace %zu < %zu bytes", ws_bytes, need);
   if (!expert_offsets || (t > 0 && (!topk_ids || !sorted_pairs)))
     return fail(WQ_ERR_ARG, "wq_moe_route: null pointer");
+  if (ws && !aligned16(ws)) return fail(WQ_ERR_ALIGN, "wq_moe_route: ws must be 16-byte aligned");
   return hip_status(wq::launch_route(topk_ids, t * topk, experts, expert_offsets, sorted_pairs,
+                                     ws && need ? static_cast<int32_t*>(ws) : nullptr,
                                      static_cast<hipStream_t>(stream)),
                     "wq_moe_route launch");
 }
@@ -530,7 +545,8 @@ wq_status moe_ffn_in(const char* what, const uint16_t* x, int64_t t, int64_t hid
   if (ws_bytes < L.bytes)
     return fail(WQ_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, L.bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = wq::launch_route(topk_ids, t * topk, (int32_t)E, L.offsets, L.sorted, s);
+  hipError_t e = wq::launch_route(topk_ids, t * topk, (int32_t)E, L.offsets, L.sorted,
+                                  L.route_table, s);
   if (e != hipSuccess) return hip_status(e, "moe ffn route");
   e = run_gate_up(x, t, L.offsets, L.sorted, topk, gate, up, L.h, s);
   if (e != hipSuccess) return hip_status(e, "moe ffn gate/up");

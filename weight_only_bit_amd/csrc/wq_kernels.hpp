@@ -64,8 +64,11 @@ hipError_t launch_gemv_moe(int fmt, int mode, const SkinnyArgs& args, int64_t ex
 hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t* out,
                           hipStream_t stream);
 
+// Entries (int32) of the per-chunk routing table a long routing array uses, 0 when the pairs
+// are sorted without one.  launch_route with table == nullptr always sorts in one workgroup.
+int64_t route_table_entries(int64_t npairs, int32_t experts);
 hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int32_t* offsets,
-                        int32_t* sorted_pairs, hipStream_t stream);
+                        int32_t* sorted_pairs, int32_t* table, hipStream_t stream);
 
 hipError_t launch_combine(const float* d, const float* weights, int64_t t, int32_t topk,
                           int64_t hidden, uint16_t* y, hipStream_t stream);

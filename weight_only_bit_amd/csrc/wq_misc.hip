@@ -107,14 +107,21 @@ __global__ __launch_bounds__(256) void dequant_alg2_kernel(const DevWeight w, in
 }
 
 // ---------------------------------------------------------------------------------------------
-// Routing: a stable counting sort of the pairs by expert, in one workgroup of T threads.
-// Thread t owns the contiguous pairs [t c, (t + 1) c) (c = ceil(npairs / T)) and a private row
-// of E counters in LDS (T * E <= 32768 int32, 128 KB):
+// Routing: a stable counting sort of the pairs by expert.  One workgroup of T threads sorts a
+// contiguous range of pairs.  Thread t owns the contiguous pairs [t c, (t + 1) c) of the range
+// (c = ceil(range / T)) and a private row of E counters in LDS (T * E <= 32768 int32, 128 KB):
 //   pass 1: each thread counts its pairs per expert in its own row (no atomics);
-//   scan:   column sums give the expert totals, their exclusive scan the expert offsets; each
-//           counter is then replaced by offsets[e] + (pairs of e owned by threads t' < t);
+//   scan:   column sums give the range's expert totals; with the whole array as the range their
+//           exclusive scan gives the expert offsets, for a chunk of a longer array the chunk's
+//           first slot per expert comes from a table (below); each counter is then replaced by
+//           that slot + (pairs of e owned by threads t' < t);
 //   pass 2: each thread walks its pairs again in order and places pair p at its counter,
 //           incrementing it -- so an expert's pairs land in increasing p.
+// Long arrays (more than two chunks of ROUTE_CHUNK_MIN pairs) are cut into chunks sorted by
+// one workgroup each: route_count_kernel writes each chunk's count per expert to a table,
+// route_scan_kernel turns the table into each chunk's first slot per expert (the column's
+// exclusive prefix plus the expert's offset) and writes the offsets, and route_kernel places
+// every chunk -- chunks in order, so the sort stays stable.
 // Ids outside [0, E) are dropped (never counted or placed), so a bad routing table cannot
 // make any kernel write out of bounds.
 // ---------------------------------------------------------------------------------------------
@@ -129,10 +136,15 @@ int route_threads(int32_t experts) {
   return p;
 }
 
+// chunk_first: null to sort the whole array in one workgroup (which then also writes the
+// offsets), else the [chunks][E] table of each chunk's first slot per expert, workgroup b
+// sorting pairs [b chunk, (b + 1) chunk).
 __global__ __launch_bounds__(ROUTE_MAX_THREADS) void route_kernel(const int32_t* __restrict__ ids,
                                                                   int64_t npairs, int32_t experts,
                                                                   int32_t* __restrict__ offsets,
-                                                                  int32_t* __restrict__ sorted) {
+                                                                  int32_t* __restrict__ sorted,
+                                                                  const int32_t* __restrict__ chunk_first,
+                                                                  int64_t chunk) {
   extern __shared__ int32_t sm[];
   const int T = blockDim.x;
   const int E = experts;
@@ -140,18 +152,27 @@ __global__ __launch_bounds__(ROUTE_MAX_THREADS) void route_kernel(const int32_t*
   const int S = T >= E ? T / E : 1;    // scan segments per expert
   const int R = T / S;                 // counter rows per segment
   int32_t* part = cnt + T * E;         // [S][E] segment sums
-  int32_t* base = part + S * E;        // [E] expert offsets
+  int32_t* base = part + S * E;        // [E] first slot of each expert in this range
   const int tid = threadIdx.x;
-  const int64_t c = (npairs + T - 1) / T;
-  const int64_t p0 = (int64_t)tid * c;
-  const int64_t p1 = p0 + c < npairs ? p0 + c : npairs;
+  const int64_t q0 = chunk_first ? (int64_t)blockIdx.x * chunk : 0;
+  const int64_t q1 = chunk_first ? (q0 + chunk < npairs ? q0 + chunk : npairs) : npairs;
+  const int64_t c = (q1 - q0 + T - 1) / T;
+  const int64_t p0 = q0 + (int64_t)tid * c;
+  const int64_t p1 = p0 + c < q1 ? p0 + c : q1;
 
   for (int i = tid; i < T * E; i += T) cnt[i] = 0;
   __syncthreads();
   int32_t* row = cnt + tid * E;
-  for (int64_t p = p0; p < p1; ++p) {
-    const int32_t e = ids[p];
-    if (e >= 0 && e < E) row[e] += 1;
+  // pairs in batches of RB: the batch's id loads are issued together, one memory round trip per
+  // batch (ids past the thread's range read as -1, which no expert matches)
+  constexpr int RB = 8;
+  for (int64_t p = p0; p < p1; p += RB) {
+    int32_t v[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) v[j] = p + j < p1 ? ids[p + j] : -1;
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+      if (v[j] >= 0 && v[j] < E) row[v[j]] += 1;
   }
   __syncthreads();
   // segment sums: (expert e, segment g) covers counter rows g R .. g R + R - 1
@@ -162,8 +183,9 @@ __global__ __launch_bounds__(ROUTE_MAX_THREADS) void route_kernel(const int32_t*
     part[g * E + e] = sum;
   }
   __syncthreads();
-  // expert totals and their exclusive scan (wave 0; lane l takes a block of experts)
-  if (tid < 64) {
+  if (chunk_first) {  // this chunk's first slots, from the table
+    for (int e = tid; e < E; e += T) base[e] = chunk_first[(int64_t)blockIdx.x * E + e];
+  } else if (tid < 64) {  // expert totals and their exclusive scan (lane l: a block of experts)
     const int per = (E + 63) / 64;
     const int e0 = tid * per;
     int32_t local = 0;
@@ -200,10 +222,90 @@ __global__ __launch_bounds__(ROUTE_MAX_THREADS) void route_kernel(const int32_t*
     }
   }
   __syncthreads();
-  for (int64_t p = p0; p < p1; ++p) {
-    const int32_t e = ids[p];
-    if (e >= 0 && e < E) sorted[row[e]++] = (int32_t)p;
+  for (int64_t p = p0; p < p1; p += RB) {
+    int32_t v[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) v[j] = p + j < p1 ? ids[p + j] : -1;
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+      if (v[j] >= 0 && v[j] < E) sorted[row[v[j]]++] = (int32_t)(p + j);
   }
+}
+
+// Chunks of a long routing array: at least ROUTE_CHUNK_MIN pairs each, at most
+// ROUTE_MAX_CHUNKS of them (the table is chunks x E int32, at most 1 MB).
+constexpr int64_t ROUTE_CHUNK_MIN = 2048;
+constexpr int64_t ROUTE_MAX_CHUNKS = 512;
+
+int64_t route_chunk(int64_t npairs) {
+  const int64_t c = (npairs + ROUTE_MAX_CHUNKS - 1) / ROUTE_MAX_CHUNKS;
+  return c > ROUTE_CHUNK_MIN ? c : ROUTE_CHUNK_MIN;
+}
+
+// Workgroup b: the per-expert counts of pairs [b chunk, (b + 1) chunk) into table row b.
+__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids,
+                                                          int64_t npairs, int32_t experts,
+                                                          int64_t chunk, int32_t* __restrict__ table) {
+  __shared__ int32_t hist[ROUTE_LDS_COUNTERS / 64];  // experts <= 512
+  const int E = experts;
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t q0 = (int64_t)blockIdx.x * chunk;
+  const int64_t q1 = q0 + chunk < npairs ? q0 + chunk : npairs;
+  for (int64_t p = q0 + threadIdx.x; p < q1; p += 256) {
+    const int32_t e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) table[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One workgroup of 512 threads (thread e: expert e): each table column becomes its exclusive
+// prefix over the chunks plus the expert's offset; the offsets are the exclusive scan of the
+// expert totals, offsets[E] the number of pairs placed.
+__global__ __launch_bounds__(512) void route_scan_kernel(int32_t* __restrict__ table,
+                                                         int32_t chunks, int32_t experts,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int32_t sc[2][512];
+  const int e = threadIdx.x;
+  const int E = experts;
+  int32_t total = 0;
+  constexpr int CB = 8;  // chunks per batch of loads
+  if (e < E) {
+    for (int b0 = 0; b0 < chunks; b0 += CB) {
+      int32_t v[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) v[j] = b0 + j < chunks ? table[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        if (b0 + j < chunks) {
+          table[(int64_t)(b0 + j) * E + e] = total;
+          total += v[j];
+        }
+    }
+  }
+  sc[0][e] = total;  // 0 for e >= E
+  __syncthreads();
+  int src = 0;
+  for (int d = 1; d < 512; d <<= 1) {  // inclusive scan over the experts
+    const int32_t v = sc[src][e] + (e >= d ? sc[src][e - d] : 0);
+    sc[src ^ 1][e] = v;
+    src ^= 1;
+    __syncthreads();
+  }
+  const int32_t first = sc[src][e] - total;
+  if (e < E) {
+    offsets[e] = first;
+    for (int b0 = 0; b0 < chunks; b0 += CB) {
+      int32_t v[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) v[j] = b0 + j < chunks ? table[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        if (b0 + j < chunks) table[(int64_t)(b0 + j) * E + e] = v[j] + first;
+    }
+  }
+  if (e == E - 1) offsets[E] = first + total;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -330,8 +432,14 @@ hipError_t launch_dequant(int fmt, const DevWeight& w, int64_t experts, uint16_t
   return hipGetLastError();
 }
 
+int64_t route_table_entries(int64_t npairs, int32_t experts) {
+  if (npairs <= 2 * ROUTE_CHUNK_MIN || experts <= 0) return 0;
+  const int64_t chunk = route_chunk(npairs);
+  return (npairs + chunk - 1) / chunk * experts;
+}
+
 hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int32_t* offsets,
-                        int32_t* sorted_pairs, hipStream_t stream) {
+                        int32_t* sorted_pairs, int32_t* table, hipStream_t stream) {
   if (experts <= 0 || experts > ROUTE_LDS_COUNTERS / 64) return hipErrorInvalidValue;
   if (npairs <= ROUTE_SMALL_PAIRS) {
     const int64_t t = npairs < 64 ? 64 : (npairs + 63) / 64 * 64;
@@ -347,8 +455,19 @@ hipError_t launch_route(const int32_t* ids, int64_t npairs, int32_t experts, int
                                     (int)(sizeof(int32_t) * (ROUTE_LDS_COUNTERS + 2 * 1024 + 512)),
                                     lds_set);
   if (e != hipSuccess) return e;
+  if (table && route_table_entries(npairs, experts) > 0) {
+    const int64_t chunk = route_chunk(npairs);
+    const int64_t chunks = (npairs + chunk - 1) / chunk;  // <= ROUTE_MAX_CHUNKS
+    hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)chunks), dim3(256), 0, stream, ids,
+                       npairs, experts, chunk, table);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(512), 0, stream, table, (int32_t)chunks,
+                       experts, offsets);
+    hipLaunchKernelGGL(route_kernel, dim3((unsigned)chunks), dim3(T), lds, stream, ids, npairs,
+                       experts, offsets, sorted_pairs, (const int32_t*)table, chunk);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(route_kernel, dim3(1), dim3(T), lds, stream, ids, npairs, experts, offsets,
-                     sorted_pairs);
+                     sorted_pairs, (const int32_t*)nullptr, (int64_t)0);
   return hipGetLastError();
 }
 
