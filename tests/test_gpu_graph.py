@@ -74,7 +74,7 @@ def test_graph_replay_gemm(wq, name, m):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("T", [6, 200])
+@pytest.mark.parametrize("T", [6, 200, 2500])  # 2500 x 2 pairs: the chunked routing sort
 def test_graph_replay_moe_ffn(wq, T):
     import torch
 
