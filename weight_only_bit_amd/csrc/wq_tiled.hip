@@ -619,19 +619,89 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the wave exits
 
   // ---- epilogue: lane holds D[m][wrow[j]] for m = 32 i + 8 q + 4 kh + t, r = 4 q + t, of each
-  // 32 x 32 tile i.  Row m's store address is a per-lane base plus m x the row stride, a
-  // uniform (scalar) product; down rows go to their pair's row of d, the pair ids of the tile's
-  // rows staged once in LDS (activation stage 0: every wave's copies have landed and its reads
-  // returned once all waves pass the barrier below), four consecutive rows per read. ----
+  // 32 x 32 tile i.  For dense products whose output rows and columns allow 16-byte pieces, the
+  // tile goes through LDS (the activation stages, free once every wave has passed the barrier
+  // below: every copy has landed and every read returned) and leaves in 16-byte stores, two
+  // rows per wave at a time -- 8 times fewer store instructions than storing each lane's bf16
+  // values.  Otherwise each lane stores its own values: row m's address is a per-lane base plus
+  // m x the row stride, a uniform (scalar) product; down rows go to their pair's row of d (pair
+  // ids staged in activation stage 0, four consecutive rows per read). ----
   const bool full_rows = rows == 32 * MT;
+  using OutT = typename std::conditional<MODE == MODE_DOWN, float, uint16_t>::type;
+  constexpr int EB = (int)sizeof(OutT);
+  constexpr int PIECE = 16 / EB;                             // elements per 16-byte piece
+  constexpr int TC = (MODE == MODE_GATEUP) ? BN / 2 : BN;    // output columns of the tile
+  constexpr int ROWB = TC * EB;                               // bytes of one output row
+  constexpr int BLKB = 32 * ROWB;                             // one 32-row block
+  constexpr int BPS = A_STAGE / BLKB;                         // blocks per activation stage
+  constexpr int BPR = NSTAGE * BPS;                           // blocks per round
+  constexpr int CPR = ROWB / 16;                              // pieces per row
+  static_assert(BPS >= 1 && A_STAGE % BLKB == 0, "output blocks must tile the stages");
+  const int64_t stride = args.out_stride;
+  // Dense products only: the MoE epilogues measured no faster this way (gate+up writes an
+  // eighth of a dense tile's bytes per lane, down's fp32 rows are scattered by pair id).
+  const bool staged = MODE == MODE_DENSE && (N % PIECE == 0) && (stride % PIECE == 0);
+  int32_t* s_pair = reinterpret_cast<int32_t*>(a_stage<0>());  // down only, never staged
+  (void)s_pair;
+  if (MODE == MODE_DOWN || staged) __syncthreads();  // every wave is done with the LDS rings
   if constexpr (MODE == MODE_DOWN) {
-    int32_t* s_pair = reinterpret_cast<int32_t*>(a_stage<0>());
-    __syncthreads();
     for (int m = tid; m < 32 * MT; m += NTHREADS)
       s_pair[m] = args.sorted_pairs[row0 + (m < rows ? m : 0)];
+  }
+  if (staged) {
+    auto blk_ptr = [&](int b) __attribute__((always_inline)) {  // block b of a round
+      const int st = b / BPS;
+      uint8_t* sb = st == 0 ? a_stage<0>() : st == 1 ? a_stage<1>() : st == 2 ? a_stage<2>() : a_stage<3>();
+      return sb + (b % BPS) * BLKB;
+    };
+    // rows 4..7 of every 8 are written 32 columns over, so the two row quads of one write
+    // (kh = 0, 1) use different banks; the pieces move whole
+    auto swz = [](int r) __attribute__((always_inline)) { return ((r >> 2) & 1) * 32; };
+#pragma unroll
+    for (int i0 = 0; i0 < MT; i0 += BPR) {
+#pragma unroll
+      for (int i = i0; i < MT && i < i0 + BPR; ++i) {
+        OutT* blk = reinterpret_cast<OutT*>(blk_ptr(i - i0));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 8 * (r >> 2) + 4 * kh + (r & 3);  // row in the block
+          if constexpr (MODE == MODE_GATEUP) {
+            const int c = (32 * wave + l32) ^ swz(rr);
+            blk[rr * TC + c] = (uint16_t)f32_to_bf16_bits(silu_f32(acc[i][0][r]) * acc[i][1][r]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int c = (64 * wave + 32 * j + l32) ^ swz(rr);
+              if constexpr (MODE == MODE_DOWN) blk[rr * TC + c] = acc[i][j][r];
+              else blk[rr * TC + c] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int nblk = (MT - i0) < BPR ? (MT - i0) : BPR;
+      for (int pc = tid; pc < nblk * 32 * CPR; pc += NTHREADS) {
+        const int rr_all = pc / CPR, ch = pc % CPR;
+        const int m = 32 * i0 + rr_all;
+        const int64_t col = n0 + (int64_t)ch * PIECE;
+        if ((!full_rows && m >= rows) || col >= N) continue;
+        const int rr = rr_all & 31;
+        const uint8_t* src = blk_ptr(rr_all >> 5) + rr * ROWB + ((ch * 16) ^ (swz(rr) * EB));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        OutT* dst;
+        if constexpr (MODE == MODE_DOWN)
+          dst = reinterpret_cast<OutT*>(args.out) + (int64_t)s_pair[m] * stride + col;
+        else
+          dst = reinterpret_cast<OutT*>(args.out) + (row0 + m) * stride + col;
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
+      if (i0 + BPR < MT) __syncthreads();  // the next round overwrites the stages
+    }
+    return;
+  }
+  if constexpr (MODE == MODE_DOWN) {
     __syncthreads();
     float* d = reinterpret_cast<float*>(args.out);
-    const int64_t stride = args.out_stride;
     const bool in0 = wrow[0] < N, in1 = wrow[1] < N;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -651,7 +721,6 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
     }
   } else {
     uint16_t* out = reinterpret_cast<uint16_t*>(args.out);
-    const int64_t stride = args.out_stride;
     uint16_t* base = out + (row0 + 4 * kh) * stride;
 #pragma unroll
     for (int j = 0; j < (MODE == MODE_GATEUP ? 1 : 2); ++j) {
