@@ -844,10 +844,10 @@ void tiled_kernel(const TiledArgs args) {
 }
 
 // One launch: the tile list holds the full tiles and every remainder tile (MoE: row_tiles
-// bounds the 256-row tiles; each expert adds at most one smaller remainder tile).
+// bounds their number, sum_e ceil(rows_e / 256); workgroups past the list exit at once).
 template <int FMT, int MODE>
 hipError_t launch_t(const TiledArgs& a, int64_t row_tiles, hipStream_t s) {
-  const int64_t tiles = (MODE == MODE_DENSE) ? a.M / BM + 1 : row_tiles + a.experts;
+  const int64_t tiles = (MODE == MODE_DENSE) ? a.M / BM + 1 : row_tiles;
   if (tiles <= 0) return hipSuccess;
   constexpr int64_t per_tile = (MODE == MODE_GATEUP) ? BN / 2 : BN;
   const int64_t cols = (a.N + per_tile - 1) / per_tile;
