@@ -40,6 +40,20 @@ def test_f32_to_bf16_matches_torch_on_every_exponent_and_rounding_case(orc):
     assert np.all(ours[nan] == 0x7FC0)
 
 
+def test_f32_to_bf16_matches_torch_on_every_fp32_pattern(orc):
+    # all 2^32 fp32 bit patterns, 2^24 at a time: round half to even on the high 16 bits, every
+    # NaN to the canonical 0x7FC0
+    low = np.arange(1 << 24, dtype=np.uint32)
+    for hi in range(256):
+        bits = low | np.uint32(hi << 24)
+        f = bits.view(np.float32)
+        ours = orc.f32_to_bf16(f)
+        ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(f)
+        assert np.array_equal(ours[~nan], ref[~nan]), hex(hi << 24)
+        assert np.all(ours[nan] == 0x7FC0), hex(hi << 24)
+
+
 def _bf16_val(b):
     return Fraction(float(orc_bits_to_f32(b)))
 
