@@ -530,6 +530,32 @@ def test_moe_prefill_skewed_routing(wq, name):
     assert_close(torch_bf16_bits(y)[tokens], ref, f"moe prefill {name}")
 
 
+@pytest.mark.parametrize("name", ["ccq", "int4", "int4pc", "affine2", "ccq432", "ccqh", "int8pc"])
+def test_moe_tiled_remainder_classes(wq, name):
+    # Experts whose routed rows hit every side of the tiled kernel's tile classes (256, 128, 64
+    # and 32 rows): remainders modulo 256 of 0, 1, 16, 17, 31, 32, 33, 64, 65, 128, 129 and 255,
+    # with and without full 256-row tiles before them; every token checked.
+    import torch
+
+    fmt, group = _fmt_group(name)
+    counts = [0, 1, 16, 17, 31, 32, 33, 64, 65, 128, 129, 255, 256, 257, 288, 289, 544, 561]
+    E, H, I, topk = len(counts), 256, 192, 2
+    flat = np.repeat(np.arange(E, dtype=np.int32), counts)
+    T = len(flat) // 2
+    assert max(counts) <= T  # pairs (flat[t], flat[t + T]) of the sorted list are distinct
+    ids = np.stack([flat[:T], flat[T:]], axis=1)
+    _, wts = synth.routing_uniform(T, topk, E, 21)
+    _say(f"moe remainder classes {name} T={T}")
+    gate = _quant(fmt, (E, I, H), (22, 1), group=group)
+    up = _quant(fmt, (E, I, H), (22, 2), group=group)
+    down = _quant(fmt, (E, H, I), (22, 3), group=group)
+    x = synth.acts_bf16((T, H), 23)
+    ref = oracle.moe_ffn(x, ids, wts, gate, up, down)
+    y = wq.wq_moe_ffn(torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(wts).cuda(), to_device(gate), to_device(up), to_device(down))
+    assert_close(torch_bf16_bits(y), ref, f"moe remainder classes {name}")
+
+
 def test_gemm_ccq_clamped_rows_bit_exact(wq):
     # Rows whose code scale / zero push the expanded code below 0 or above 2^15 - 1 (and rows
     # that stay inside, in the same 16-row tile): the product path's decode must still equal
