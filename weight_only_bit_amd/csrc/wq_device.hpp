@@ -16,6 +16,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 enum { FMT_INT4 = 1, FMT_AFFINE2 = 2, FMT_CCQ2 = 3, FMT_CCQ432 = 4, FMT_CCQH = 5, FMT_INT8 = 6 };
 

@@ -641,12 +641,15 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   // Dense products only: the MoE epilogues measured no faster this way (gate+up writes an
   // eighth of a dense tile's bytes per lane, down's fp32 rows are scattered by pair id).
   const bool staged = MODE == MODE_DENSE && (N % PIECE == 0) && (stride % PIECE == 0);
-  int32_t* s_pair = reinterpret_cast<int32_t*>(a_stage<0>());  // down only, never staged
-  (void)s_pair;
+  // down only (never staged): the address of each tile row's row of d (its pair's row)
+  uint64_t* s_row = reinterpret_cast<uint64_t*>(a_stage<0>());
+  (void)s_row;
   if (MODE == MODE_DOWN || staged) __syncthreads();  // every wave is done with the LDS rings
   if constexpr (MODE == MODE_DOWN) {
     for (int m = tid; m < 32 * MT; m += NTHREADS)
-      s_pair[m] = args.sorted_pairs[row0 + (m < rows ? m : 0)];
+      s_row[m] = reinterpret_cast<uint64_t>(
+          reinterpret_cast<float*>(args.out) +
+          (int64_t)args.sorted_pairs[row0 + (m < rows ? m : 0)] * stride);
   }
   if (staged) {
     auto blk_ptr = [&](int b) __attribute__((always_inline)) {  // block b of a round
@@ -690,7 +693,7 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
         const u32x4 v = *reinterpret_cast<const u32x4*>(src);
         OutT* dst;
         if constexpr (MODE == MODE_DOWN)
-          dst = reinterpret_cast<OutT*>(args.out) + (int64_t)s_pair[m] * stride + col;
+          dst = reinterpret_cast<OutT*>(s_row[m]) + col;
         else
           dst = reinterpret_cast<OutT*>(args.out) + (row0 + m) * stride + col;
         *reinterpret_cast<u32x4*>(dst) = v;
@@ -699,46 +702,84 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
     }
     return;
   }
+  // Full tiles whose rows all exist and whose wave's columns all lie inside N (uniform per
+  // wave) store without per-element checks; ragged ones check every row and column.
+  constexpr int WCOLS = (MODE == MODE_GATEUP) ? 32 : 64;  // output columns of one wave
+  const bool wave_cols = n0 + WCOLS * (wave + 1) <= N;
   if constexpr (MODE == MODE_DOWN) {
     __syncthreads();
-    float* d = reinterpret_cast<float*>(args.out);
-    const bool in0 = wrow[0] < N, in1 = wrow[1] < N;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m0 = 32 * i + 8 * q + 4 * kh;
-        const int4 pr = *reinterpret_cast<const int4*>(s_pair + m0);
-        const int32_t pid[4] = {pr.x, pr.y, pr.z, pr.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (!full_rows && m0 + t >= rows) continue;
-          float* drow = d + (int64_t)pid[t] * stride;
-          if (in0) drow[wrow[0]] = acc[i][0][4 * q + t];
-          if (in1) drow[wrow[1]] = acc[i][1][4 * q + t];
-        }
-      }
-    }
-  } else {
-    uint16_t* out = reinterpret_cast<uint16_t*>(args.out);
-    uint16_t* base = out + (row0 + 4 * kh) * stride;
-#pragma unroll
-    for (int j = 0; j < (MODE == MODE_GATEUP ? 1 : 2); ++j) {
-      const int64_t n = wrow[j];
-      if (n >= N) continue;
+    auto store_rows = [&](auto checked) __attribute__((always_inline)) {
+      constexpr bool CK = decltype(checked)::value;
+      const bool in0 = wrow[0] < N, in1 = wrow[1] < N;
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
+        // the addresses of the lane's 16 rows of block i (rows 32 i + 8 q + 4 kh + t), read
+        // before the block's first store
+        uint64_t ra[4][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mc = 32 * i + 8 * (r >> 2) + (r & 3);  // m - 4 kh: the uniform part of the row
-          if (!full_rows && mc + 4 * kh >= rows) continue;
-          float v;
-          if constexpr (MODE == MODE_GATEUP) {
-            v = silu_f32(acc[i][0][r]) * acc[i][1][r];
-          } else {
-            v = acc[i][j][r];
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = 32 * i + 8 * q + 4 * kh;
+          const u64x2 a01 = *reinterpret_cast<const u64x2*>(s_row + m0);
+          const u64x2 a23 = *reinterpret_cast<const u64x2*>(s_row + m0 + 2);
+          ra[q][0] = a01.x;
+          ra[q][1] = a01.y;
+          ra[q][2] = a23.x;
+          ra[q][3] = a23.y;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m0 = 32 * i + 8 * q + 4 * kh;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (CK && m0 + t >= rows) continue;
+            // a global-memory pointer (the generic form would compile to flat stores)
+            __attribute__((address_space(1))) float* drow =
+                reinterpret_cast<__attribute__((address_space(1))) float*>(ra[q][t]);
+            if (!CK || in0) drow[wrow[0]] = acc[i][0][4 * q + t];
+            if (!CK || in1) drow[wrow[1]] = acc[i][1][4 * q + t];
           }
-          base[(int64_t)mc * stride + n] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    };
+    if (full_rows && wave_cols) store_rows(std::false_type{});
+    else store_rows(std::true_type{});
+  } else {
+    uint16_t* out = reinterpret_cast<uint16_t*>(args.out);
+    auto value = [&](int i, int j, int r) __attribute__((always_inline)) {
+      if constexpr (MODE == MODE_GATEUP) return silu_f32(acc[i][0][r]) * acc[i][1][r];
+      else return acc[i][j][r];
+    };
+    // Fast path: row m = 32 i + 8 (r / 4) + 4 kh + r % 4 of the tile at a uniform row address
+    // (rows 32 i + 8 (r / 4) + r % 4) plus the lane's byte offset 2 (4 kh stride + n), which
+    // fits 32 bits when 4 stride + N < 2^30.
+    if (full_rows && wave_cols && 4 * stride + N < (1ll << 30)) {
+#pragma unroll
+      for (int j = 0; j < (MODE == MODE_GATEUP ? 1 : 2); ++j) {
+        const uint32_t loff = (uint32_t)(2 * (4 * kh * stride + wrow[j]));
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int mc = 32 * i + 8 * (r >> 2) + (r & 3);
+            uint8_t* rowp = reinterpret_cast<uint8_t*>(out + (row0 + mc) * stride);
+            *reinterpret_cast<uint16_t*>(rowp + loff) = (uint16_t)f32_to_bf16_bits(value(i, j, r));
+          }
+        }
+      }
+    } else {
+      uint16_t* base = out + (row0 + 4 * kh) * stride;
+#pragma unroll
+      for (int j = 0; j < (MODE == MODE_GATEUP ? 1 : 2); ++j) {
+        const int64_t n = wrow[j];
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int mc = 32 * i + 8 * (r >> 2) + (r & 3);  // m - 4 kh: the uniform part of the row
+            if (!full_rows && mc + 4 * kh >= rows) continue;
+            base[(int64_t)mc * stride + n] = (uint16_t)f32_to_bf16_bits(value(i, j, r));
+          }
         }
       }
     }
