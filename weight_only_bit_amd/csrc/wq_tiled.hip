@@ -800,11 +800,7 @@ void tiled_kernel(const TiledArgs args) {
     sC2 = sC2_;
     sC3 = sC3_;
   }
-  // The MoE tile lookup result lives in the first bytes of packed-data stage 1 (INT8's rings
-  // fill the LDS exactly); every thread has read it before any copy writes that stage.
-  int32_t* s_tile = reinterpret_cast<int32_t*>(sC1);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
 
   // ---- which tile: XCD-aware order ----
   // Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD w % 8).  Row tile
@@ -833,47 +829,52 @@ void tiled_kernel(const TiledArgs args) {
     }
     rows = args.M - row0 < BM ? args.M - row0 : BM;
   } else {
-    if (tid < 64) {  // wave 0: per-expert tile counts, scanned 64 experts at a time
-      int64_t idx = rtile;
-      int found_e = -1, found_c = 0, local = 0;
+    // Every wave finds the tile itself (the same uniform result in each, no LDS, no barrier):
+    // per-expert tile counts of each size class, scanned 64 experts at a time.  With at most
+    // 64 experts the counts are loaded once.
+    int64_t idx = rtile;
+    int found_e = -1, found_c = 0, local = 0;
+    auto find = [&](int32_t nt, int cls, int eb) __attribute__((always_inline)) {
+      int32_t incl = nt;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int32_t v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+      }
+      const int32_t total = __shfl(incl, 63);
+      if (idx < total) {
+        const uint64_t m = __ballot(idx >= incl - nt && idx < incl);
+        const int src = __ffsll((unsigned long long)m) - 1;
+        found_e = eb + src;
+        found_c = cls;
+        local = (int)(idx - __shfl(incl - nt, src));
+      } else {
+        idx -= total;
+      }
+    };
+    if (args.experts <= 64) {
+      const int64_t cnt = lane < args.experts ? args.offsets[lane + 1] - args.offsets[lane] : 0;
+      for (int ci = 0; ci < 4 && found_e < 0; ++ci)
+        find((int32_t)class_tiles(8 >> ci, cnt), 8 >> ci, 0);
+    } else {
       for (int ci = 0; ci < 4 && found_e < 0; ++ci) {
         const int cls = 8 >> ci;
         for (int eb = 0; eb < args.experts && found_e < 0; eb += 64) {
           const int ex = eb + lane;
-          int32_t nt = 0;
-          if (ex < args.experts) nt = (int32_t)class_tiles(cls, args.offsets[ex + 1] - args.offsets[ex]);
-          int32_t incl = nt;
-          for (int d = 1; d < 64; d <<= 1) {
-            const int32_t v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-          }
-          const int32_t total = __shfl(incl, 63);
-          if (idx < total) {
-            const uint64_t m = __ballot(idx >= incl - nt && idx < incl);
-            const int src = __ffsll((unsigned long long)m) - 1;
-            found_e = eb + src;
-            found_c = cls;
-            local = (int)(idx - __shfl(incl - nt, src));
-          } else {
-            idx -= total;
-          }
+          const int32_t nt =
+              ex < args.experts ? (int32_t)class_tiles(cls, args.offsets[ex + 1] - args.offsets[ex]) : 0;
+          find(nt, cls, eb);
         }
       }
-      if (lane == 0) {
-        s_tile[0] = found_e;
-        s_tile[1] = found_c;
-        s_tile[2] = local;
-      }
     }
-    __syncthreads();
-    if (s_tile[0] < 0) return;
-    e = s_tile[0];
-    mt = s_tile[1];
+    found_e = __builtin_amdgcn_readfirstlane(found_e);
+    if (found_e < 0) return;
+    e = found_e;
+    mt = __builtin_amdgcn_readfirstlane(found_c);
+    local = __builtin_amdgcn_readfirstlane(local);
     const int64_t base = args.offsets[e];
     const int64_t cnt = args.offsets[e + 1] - base;
-    row0 = base + class_row0(mt, cnt, s_tile[2]);
+    row0 = base + class_row0(mt, cnt, local);
     rows = base + cnt - row0 < BM ? base + cnt - row0 : BM;
-    __syncthreads();  // s_tile read by every thread before stage 1 is overwritten
   }
   const CodeStages cs{{sC0, sC1, sC2, sC3}};
   switch (mt) {
