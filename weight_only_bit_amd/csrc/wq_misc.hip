@@ -386,7 +386,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
 
 // ---------------------------------------------------------------------------------------------
 // Combine: y[t][c] = bf16( sum_j w[t][j] * d[t*topk + j][c] ), slots summed in order j with
-// fp32 fused multiply-adds.  One thread per 4 columns.
+// fp32 fused multiply-adds.  One thread per 4 columns; the slots' rows are loaded 8 at a time
+// before their multiply-adds, so a thread has up to 8 loads in flight.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ d,
                                                       const float* __restrict__ wts, int64_t t,
@@ -398,13 +399,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int64_t tok = q / quads;
   const int64_t c = (q % quads) * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const float w = wts[tok * topk + j];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(d + (tok * topk + j) * hidden + c);
-    acc.x = __builtin_fmaf(w, v.x, acc.x);
-    acc.y = __builtin_fmaf(w, v.y, acc.y);
-    acc.z = __builtin_fmaf(w, v.z, acc.z);
-    acc.w = __builtin_fmaf(w, v.w, acc.w);
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    float w[8];
+    f32x4 v[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int64_t j = j0 + jj;
+      if (j < topk) {
+        w[jj] = wts[tok * topk + j];
+        v[jj] = *reinterpret_cast<const f32x4*>(d + (tok * topk + j) * hidden + c);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < topk) {
+        acc.x = __builtin_fmaf(w[jj], v[jj].x, acc.x);
+        acc.y = __builtin_fmaf(w[jj], v[jj].y, acc.y);
+        acc.z = __builtin_fmaf(w[jj], v[jj].z, acc.z);
+        acc.w = __builtin_fmaf(w[jj], v[jj].w, acc.w);
+      }
+    }
   }
   u32x2 o = {pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
   *reinterpret_cast<u32x2*>(y + tok * hidden + c) = o;
