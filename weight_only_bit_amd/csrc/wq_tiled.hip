@@ -213,50 +213,66 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   //   dense/down: channel n0 + 64 wave + 32 j + l32
   //   gate+up: j = 0 -> gate row n0 + 32 wave + l32, j = 1 -> the matching up row
   // i.e. "wave row" 32 j + l32 of the wave's 64 rows.  Copy: lane l copies wave row l.
+  // The rows' constants are loaded here and scaled only after the prologue has issued its
+  // packed-data copies: an operation on a loaded value makes the wave wait for the load first.
   using Ring = CodeRing<FMT>;
   int64_t wrow[2];
   RowConst rc[2];
+  float rl[2][3] = {{0.f, 0.f, 0.f}, {0.f, 0.f, 0.f}};  // CCQ: code scale, code zero, super scale
+  uint32_t rb[2] = {0u, 0u};                             // INT8: the row's scale (bf16 bits)
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     wrow[j] = (MODE == MODE_GATEUP) ? n0 + 32 * wave + l32 : n0 + 64 * wave + 32 * j + l32;
-    rc[j] = RowConst{0.f, 0.f, 0.f};
     if constexpr (FMT == FMT_CCQ2) {
       const DevWeight& w = (MODE == MODE_GATEUP && j == 1) ? args.w1 : args.w0;
       const int64_t grow = e * w.n + (wrow[j] < N ? wrow[j] : N - 1);
-      rc[j] = RowConst{w.code_scale[grow] * kTwo24, w.code_zero[grow], w.super_scale[grow] * kTwo24};
+      rl[j][0] = w.code_scale[grow];
+      rl[j][1] = w.code_zero[grow];
+      rl[j][2] = w.super_scale[grow];
     } else if constexpr (FMT == FMT_INT8) {  // the row's one scale
       const DevWeight& w = (MODE == MODE_GATEUP && j == 1) ? args.w1 : args.w0;
       const int64_t grow = e * w.n + (wrow[j] < N ? wrow[j] : N - 1);
-      rc[j] = RowConst{0.f, 0.f, bf16_bits_to_f32(w.scales[grow]) * kTwo24};
+      rb[j] = w.scales[grow];
     }
   }
   const float mzp24 = -(float)args.w0.zp / kTwo24;
   RowSrc rs;
-  float own_fin24 = 0.f;  // (4,3,2) / hybrid: super scale * 2^24 of wave row `lane`
+  float own_super = 0.f;  // (4,3,2) / hybrid: super scale of wave row `lane`
+  float own_fin24 = 0.f;  // ... times 2^24
   {
     const int jj = lane >> 5;  // wave row `lane` = 32 jj + (lane % 32)
     const int64_t r = (MODE == MODE_GATEUP) ? n0 + 32 * wave + (lane & 31)
                                             : n0 + 64 * wave + lane;
     const DevWeight& w = (MODE == MODE_GATEUP && jj == 1) ? args.w1 : args.w0;
     rs = row_src<FMT>(w, e, r < N ? r : N - 1);
-    if constexpr (is_alg2(FMT)) own_fin24 = w.super_scale[e * w.n + (r < N ? r : N - 1)] * kTwo24;
+    if constexpr (is_alg2(FMT)) own_super = w.super_scale[e * w.n + (r < N ? r : N - 1)];
   }
+  auto scale_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (FMT == FMT_CCQ2) rc[j] = RowConst{rl[j][0] * kTwo24, rl[j][1], rl[j][2] * kTwo24};
+      else if constexpr (FMT == FMT_INT8) rc[j] = RowConst{0.f, 0.f, bf16_bits_to_f32(rb[j]) * kTwo24};
+      else rc[j] = RowConst{0.f, 0.f, 0.f};
+    }
+    own_fin24 = own_super * kTwo24;
+  };
 
   // ---- activation copy role ----
   // Copy instruction i of wave w fills rows 32 i + 8 w .. + 7 of a stage (1 KB: lane l lands
   // at byte 16 l); lane l's row is r = 32 i + 8 w + l / 8 and its slot l % 8 receives piece
   // (l % 8) ^ ((r / 2) % 8) = (l % 8) ^ ((4 w + l / 16) % 8) of that row.  Rows past the end of a ragged tile read the tile's first
   // row; their results are never stored.
+  // Gate+up rows are tokens: the pair ids are loaded here and turned into row addresses only
+  // after the prologue has issued its packed-data copies, which need no wait for them.
   const uint16_t* csrc[MT];
-  {
-    const int piece = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  int32_t pair[MT];
+  const int piece = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int r = 32 * i + 8 * wave + (lane >> 3);
-      const int64_t gr = row0 + (r < rows ? r : 0);
-      const int64_t src = (MODE == MODE_GATEUP) ? (int64_t)(args.sorted_pairs[gr] / args.topk) : gr;
-      csrc[i] = args.a + src * args.a_stride + piece * 8;
-    }
+  for (int i = 0; i < MT; ++i) {
+    const int r = 32 * i + 8 * wave + (lane >> 3);
+    const int64_t gr = row0 + (r < rows ? r : 0);
+    if constexpr (MODE == MODE_GATEUP) pair[i] = args.sorted_pairs[gr];
+    else csrc[i] = args.a + gr * args.a_stride + piece * 8;
   }
   auto copy_a = [&](int64_t g, auto stc) __attribute__((always_inline)) {
     uint8_t* base = a_stage<decltype(stc)::value>();
@@ -507,12 +523,20 @@ __device__ __forceinline__ void tile_body(const TiledArgs& args, const CodeStage
   constexpr int CD = Ring::DEPTH;
 
   // ---- prologue: steps 0 and 1 of the activations and 0..AHEAD-1 of the packed data in
-  // flight, step 0 decoded and visible ----
+  // flight, step 0 decoded and visible.  The packed data (from HBM, addresses known at once)
+  // goes first; the activation copies may wait for the pair ids that locate their rows. ----
   copy_codes(0, std::integral_constant<int, 0>{});
-  copy_a(0, std::integral_constant<int, 0>{});
   copy_codes(clamp_step(1), std::integral_constant<int, 1 % CD>{});
-  copy_a(clamp_step(1), std::integral_constant<int, 1>{});
   if constexpr (Ring::AHEAD > 2) copy_codes(clamp_step(2), std::integral_constant<int, 2 % CD>{});
+  __builtin_amdgcn_sched_barrier(0);
+  scale_rows();
+  if constexpr (MODE == MODE_GATEUP) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      csrc[i] = args.a + (int64_t)(pair[i] / args.topk) * args.a_stride + piece * 8;
+  }
+  copy_a(0, std::integral_constant<int, 0>{});
+  copy_a(clamp_step(1), std::integral_constant<int, 1>{});
   __builtin_amdgcn_s_waitcnt(0);  // everything issued so far
   __syncthreads();
   decode_step(0, std::integral_constant<int, 0>{}, Bw[0]);
