@@ -556,6 +556,84 @@ def test_moe_tiled_remainder_classes(wq, name):
     assert_close(torch_bf16_bits(y), ref, f"moe remainder classes {name}")
 
 
+def _bf16(v):
+    """bf16 bits of a value that bf16 holds exactly."""
+    b = int(np.array(v, np.float32).view(np.uint32))
+    assert b & 0xFFFF == 0, v
+    return b >> 16
+
+
+_BF16_MAX = float(np.array(0x7F7F0000, np.uint32).view(np.float32))
+# (a, b, bf16 bits of the correctly rounded a + b): pairs of bf16 values whose fp32 sum is exact
+# and lies on or next to a bf16 rounding boundary.
+ROUNDING_PAIRS = [
+    (1.0, 2.0 ** -8, 0x3F80),                  # tie: down to the even 1.0
+    (1.0 + 2.0 ** -7, 2.0 ** -8, 0x3F82),      # tie: up to the even 1 + 2^-6
+    (1.0, 2.0 ** -8 + 2.0 ** -15, 0x3F81),     # just above the tie: up
+    (1.0, 3 * 2.0 ** -9, 0x3F81),              # above the tie: up
+    (-1.0, -(2.0 ** -8), 0xBF80),              # negative tie: down in magnitude
+    (-(1.0 + 2.0 ** -7), -(2.0 ** -8), 0xBF82),
+    (2.0 - 2.0 ** -7, 2.0 ** -8, 0x4000),      # tie at the top of a binade: carries to 2
+    (256.0, 1.0, 0x4380), (258.0, 1.0, 0x4382),  # ties where the bf16 step is 2
+    (3.0, -3.0, 0x0000),                       # exact cancellation: +0
+    (_BF16_MAX, 2.0 ** 119, 0x7F80),           # tie above the largest bf16: +inf
+    (-_BF16_MAX, -(2.0 ** 119), 0xFF80),       # and -inf
+    (1.5, 0.0, 0x3FC0),                        # exact
+]
+
+
+@pytest.mark.parametrize("n", [64, 60])
+@pytest.mark.parametrize("m", [1, 9, 24, 40, 300])
+def test_products_round_half_to_even_bit_exact(wq, m, n):
+    # The output rounding of every product kernel (single-staging up to 16 rows, chunked up to
+    # 32, tiled beyond; n = 60 takes the tiled kernel's register epilogue, 64 its staged one),
+    # bit for bit: every weight is exactly 1 and row i of x holds a pair (a, b) in columns 0
+    # and 1, so y[i][c] = bf16(a + b) for every column c.
+    import torch
+
+    k = 256
+    p = oracle.Packed(oracle.INT8, n, k, 1, 0, np.ones((1, n, k), np.uint8),
+                      np.full((1, n), 0x3F80, np.uint16))
+    assert np.all(oracle.dequantize(p) == 0x3F80)
+    x = np.zeros((m, k), np.uint16)
+    want = np.zeros(m, np.uint16)
+    for i in range(m):
+        a, b, r = ROUNDING_PAIRS[i % len(ROUNDING_PAIRS)]
+        x[i, 0], x[i, 1], want[i] = _bf16(a), _bf16(b), r
+    ref = oracle.gemm(x, p)
+    assert np.array_equal(ref, np.repeat(want[:, None], n, axis=1))
+    y = torch_bf16_bits(wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), to_device(p)))
+    assert np.array_equal(y, ref), np.argwhere(y != ref)[:5]
+
+
+def test_combine_rounds_like_the_oracle(wq):
+    # wq_moe_combine with one slot of weight 1 returns bf16(1 * d + 0): checked bit for bit
+    # against the oracle's fp32 -> bf16 conversion on random fp32 patterns (subnormals left
+    # out), every rounding tie class of the low half, infinities, zeros and NaNs with payloads
+    # (all to 0x7FC0).
+    import torch
+
+    g = np.random.default_rng(41)
+    bits = g.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    hi = g.integers(0, 1 << 16, 4096, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], np.uint32)
+    special = np.array([0x7F800000, 0xFF800000, 0x00000000, 0x80000000, 0x7FC00000,
+                        0xFFC00001, 0x7F800001, 0x7FBFFFFF, 0x7F7FFFFF, 0x7F7F8000], np.uint32)
+    bits = np.concatenate([bits, (hi[:, None] | lows[None, :]).ravel(), special])
+    expo = (bits >> 23) & 0xFF
+    bits = bits[(expo != 0) | ((bits & 0x7FFFFF) == 0)]  # no subnormals
+    hidden = 4096
+    bits = np.resize(bits, (bits.size + hidden - 1) // hidden * hidden)
+    d = bits.view(np.float32).reshape(-1, hidden)
+    t = d.shape[0]
+    w = np.ones((t, 1), np.float32)
+    with np.errstate(invalid="ignore"):
+        want = oracle.f32_to_bf16(d * np.float32(1.0) + np.float32(0.0))
+    y = torch_bf16_bits(wq.wq_moe_combine(torch.from_numpy(d.copy()).cuda(),
+                                          torch.from_numpy(w).cuda()))
+    assert np.array_equal(y, want), np.argwhere(y != want)[:5]
+
+
 def test_gemm_ccq_clamped_rows_bit_exact(wq):
     # Rows whose code scale / zero push the expanded code below 0 or above 2^15 - 1 (and rows
     # that stay inside, in the same 16-row tile): the product path's decode must still equal

@@ -45,16 +45,27 @@ struct DevWeight {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// fp32 -> bf16 bits, round half to even; NaN -> 0x7FC0.
+// Two fp32 values -> packed bf16 pair, low half first (v_cvt_pk_bf16_f32: round half to even;
+// a NaN keeps its sign and payload bits).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// fp32 -> bf16 bits, round half to even; NaN -> 0x7FC0.  On any other input the conversion
+// instruction gives (u + 0x7FFF + ((u >> 16) & 1)) >> 16 of the bit pattern u; a NaN is
+// replaced by the canonical one.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t b = cvt_pk_bf16(f, f) & 0xFFFFu;
+  return f != f ? 0x7FC0u : b;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  uint32_t p = cvt_pk_bf16(lo, hi);
+  if (lo != lo) p = (p & 0xFFFF0000u) | 0x7FC0u;
+  if (hi != hi) p = (p & 0x0000FFFFu) | 0x7FC00000u;
+  return p;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -77,13 +88,6 @@ __device__ __forceinline__ uint32_t ccq_expand_bits(float cprime, float cscale, 
 __device__ __forceinline__ bool ccq_row_needs_no_clamp(float cscale, float czero) {
   const float a = __builtin_fmaf(0.0f, cscale, czero), b = __builtin_fmaf(255.0f, cscale, czero);
   return fminf(a, b) >= 0.0f && fmaxf(a, b) <= 32767.0f;
-}
-
-// Two fp32 values -> packed bf16 pair (round half to even), low half first.
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------------------------
