@@ -162,3 +162,48 @@ def test_moe_pages_grouped_shape(wq, name, tokens):
     x = synth.acts_bf16((tokens, hidden), 843, tokens)
     ids, wts = synth.routing_uniform(tokens, 8, n_exp, 844, tokens)
     _check_tokens(wq, mats, x, ids, wts, np.arange(tokens), f"pages grouped {name} t={tokens}")
+
+
+# The pages' GEMV operator shapes (CCQ paper, section 5, GEMV table: input 4096 or 8192,
+# output 1024, 4096 or 8192, one and four rows), in the two 2-bit formats the table compares;
+# the seeded random packed bytes of synth (the layout and magnitudes of quantized weights),
+# every output against the oracle.
+PAGES_GEMV = [(4096, 4096), (4096, 1024), (8192, 8192), (8192, 1024)]
+
+
+@pytest.mark.parametrize("k,n", PAGES_GEMV)
+@pytest.mark.parametrize("fmt_name", ["affine2", "ccq"])
+def test_pages_gemv_shapes(wq, k, n, fmt_name):
+    import torch
+
+    fmt = {"affine2": oracle.AFFINE2, "ccq": oracle.CCQ}[fmt_name]
+    arr = synth.random_packed(fmt, 1, n, k, 850, k, n)
+    p = oracle.Packed(fmt, n, k, 1, 64, arr["codes"], arr.get("scales"), arr.get("zeros"),
+                      arr.get("qscale"), arr.get("super_scale"), arr.get("code_scale"),
+                      arr.get("code_zero"), oracle.default_zp(fmt))
+    w = to_device(p)
+    for m in (1, 4):
+        _say(f"pages gemv {fmt_name} k={k} n={n} m={m}")
+        x = synth.acts_bf16((m, k), 851, k, n, m)
+        y = wq.wq_gemm(torch.from_numpy(x.view(np.int16)).cuda(), w)
+        assert_close(torch_bf16_bits(y), oracle.gemm(x, p), f"pages gemv {fmt_name} {k}x{n} m={m}")
+
+
+# The pages' grouped-GEMM shape at the table's larger token counts (16 and 64 tokens, 8 of 256
+# experts each), CCQ and W8A16 (INT8 per channel): every token against the oracle.
+@pytest.mark.parametrize("name,tokens", [("ccq", 16), ("int8pc", 16), ("ccq", 64)])
+def test_moe_pages_grouped_shape_more_tokens(wq, name, tokens):
+    fmt, group = {"ccq": (oracle.CCQ, 64), "int8pc": (oracle.INT8, 0)}[name]
+    n_exp, hidden, inter = 256, 7168, 512
+    _say(f"pages grouped shape {name} tokens={tokens}: drawing weights")
+    mats = []
+    for j, (n, k) in enumerate(((inter, hidden), (inter, hidden), (hidden, inter))):
+        arr = synth.random_packed_device(fmt, n_exp, n, k, 860 + j, group=group)
+        mats.append(wq.PackedWeight(fmt, n, k, n_exp, group,
+                                    *(arr.get(f) for f in ("codes", "scales", "zeros", "qscale",
+                                                            "super_scale", "code_scale",
+                                                            "code_zero")),
+                                    oracle.default_zp(fmt)))
+    x = synth.acts_bf16((tokens, hidden), 863, tokens)
+    ids, wts = synth.routing_uniform(tokens, 8, n_exp, 864, tokens)
+    _check_tokens(wq, mats, x, ids, wts, np.arange(tokens), f"pages grouped {name} t={tokens}")
