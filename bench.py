@@ -498,7 +498,9 @@ def dense_decode(args):
     """One 4096 x 4096 linear at 1, 8 and 32 rows, CCQ, 2-bit affine and WINT8 (per channel, the
     deployment's dense layers); each call reads one of
     enough distinct weight copies (>= 1 GiB in total) that the 256 MB last-level cache holds no
-    weights between calls."""
+    weights between calls.  Also the 512 x 512 W4A16 linear (INT4 g64) at 1 and 8 rows over
+    >= 512 MB of copies, and for every case a "hot" time: one copy called again and again, its
+    weights in cache."""
     import numpy as np
     import torch
 
@@ -526,14 +528,32 @@ def dense_decode(args):
             y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
             us, eager = graph_us(lambda i: wq.wq_gemm(x, copies[i % len(copies)], y=y), len(copies),
                                  max(args.steps, 1))
+            hot, _ = graph_us(lambda i: wq.wq_gemm(x, copies[0], y=y), 256, max(args.steps, 1))
             res[f"{name}_m{m}"] = {"us": round(us, 2), "GB/s": round(one / (us * 1e-6) / 1e9, 1),
-                                   "eager_us": round(eager, 2)}
+                                   "eager_us": round(eager, 2), "hot_us": round(hot, 2)}
+        del copies
+    # W4A16 512 x 512: the copies are views into one [R, 512, 512] packed array
+    n1 = k1 = 512
+    one1 = n1 * k1 // 2 + n1 * (k1 // 64) * 2
+    R = -(-(512 << 20) // one1)
+    arr = synth.random_packed_device(wq.FMT_INT4, R, n1, k1, 3500, group=64)
+    c1 = [wq.PackedWeight(wq.FMT_INT4, n1, k1, 1, 64, arr["codes"][i:i + 1], arr["scales"][i:i + 1],
+                          None, None, None, None, None, 8) for i in range(R)]
+    for m in (1, 8):
+        x = torch.from_numpy(synth.acts_bf16((m, k1), 503, m).view(np.int16)).to(dev)
+        y = torch.empty((m, n1), dtype=torch.bfloat16, device=dev)
+        us, eager = graph_us(lambda i: wq.wq_gemm(x, c1[i], y=y), R, max(args.steps, 1))
+        hot, _ = graph_us(lambda i: wq.wq_gemm(x, c1[0], y=y), 256, max(args.steps, 1))
+        res[f"w4a16_512_m{m}"] = {"us": round(us, 2), "GB/s": round(one1 / (us * 1e-6) / 1e9, 1),
+                                  "eager_us": round(eager, 2), "hot_us": round(hot, 2)}
     out = {"metric": "weight-stream GB/s, dense 4096x4096 linear", "value": res["ccq_m1"]["GB/s"],
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "dense_decode", "n": N, "k": Kd}, "results": res,
-           "note": "us: per call from HIP-graph replay of the calls (no host launch cost); "
-                   "eager_us: the same calls launched one by one from Python"}
+           "note": "us: per call from HIP-graph replay of the calls (no host launch cost), each "
+                   "call on a weight copy not in cache; eager_us: the same calls launched one by "
+                   "one from Python; hot_us: graph replay of one copy called again and again "
+                   "(weights in cache); w4a16_512: the 512 x 512 INT4 g64 linear"}
     print(json.dumps(out), flush=True)
 
 
