@@ -79,6 +79,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baselines."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def omp_threads(n):
+    """Set the OpenMP thread count of this thread's later parallel regions (the oracle's)."""
+    import ctypes
+
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
 # --wformat name -> (wq format id, zero point, label)
 WFORMATS = {"ccq": (3, 32, "CCQ (6,4,3) code cluster g64"),
             "ccq432": (4, 8, "CCQ (4,3,2) g64"),
@@ -275,6 +294,7 @@ def main():
             errs.append(assert_close(torch_bf16_bits(ys[l])[toks], yref, f"bench spot parity layer {l}"))
             log(f"oracle layer {l}: {len(toks)} token(s) in {tot_s:.1f} s cumulative")
         cpu = {"value": round(tot_bytes / tot_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "cpu_model": cpu_model(),
                "kind": "oracle",
                "sample": f"{args.cpu_tokens} token(s) of layer(s) {sample_layers} "
                          f"(CCQ and INT4 per-channel), all 8 routed experts decoded and multiplied; "
@@ -424,7 +444,8 @@ def prefill_measure(args, wq, synth, dev, cpu_tokens=0):
         err = assert_close(torch_bf16_bits(y)[toks], yref, "bench prefill spot parity")
         res["cpu_baseline"] = {
             "value": round(2.0 * len(toks) * K * 3 * H * I / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{len(toks)} token(s) of the prefill layer (each with its 8 routed experts "
                       f"decoded and multiplied), {dt:.1f} s"}
         res["spot_parity_max_rel_err"] = err
@@ -546,10 +567,37 @@ def dense_decode(args):
         hot, _ = graph_us(lambda i: wq.wq_gemm(x, c1[0], y=y), 256, max(args.steps, 1))
         res[f"w4a16_512_m{m}"] = {"us": round(us, 2), "GB/s": round(one1 / (us * 1e-6) / 1e9, 1),
                                   "eager_us": round(eager, 2), "hot_us": round(hot, 2)}
+    # The oracle on the host (context only): one row of each linear, all threads and one.
+    import oracle
+
+    cpu = {}
+    ncores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    for name, fmt, n, k in (("ccq_m1", oracle.CCQ, 4096, 4096), ("w4a16_512_m1", oracle.INT4, 512, 512)):
+        a = synth.random_packed(fmt, 1, n, k, 3600)
+        pk = oracle.Packed(fmt, n, k, 1, 64, a["codes"], a.get("scales"), a.get("zeros"), a.get("qscale"),
+                           a.get("super_scale"), a.get("code_scale"), a.get("code_zero"),
+                           oracle.default_zp(fmt))
+        xh = synth.acts_bf16((1, k), 504)
+        nbytes = sum(v.nbytes for v in a.values())
+        row = {}
+        for threads in (ncores, 1):
+            omp_threads(threads)
+            oracle.gemm(xh, pk)
+            calls, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < 1.0:
+                oracle.gemm(xh, pk)
+                calls += 1
+            s = (time.perf_counter() - t0) / calls
+            row[f"{threads}_threads"] = {"us": round(s * 1e6, 1), "GB/s": round(nbytes / s / 1e9, 3)}
+        omp_threads(ncores)
+        cpu[name] = row
     out = {"metric": "weight-stream GB/s, dense 4096x4096 linear", "value": res["ccq_m1"]["GB/s"],
            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "dense_decode", "n": N, "k": Kd}, "results": res,
+           "cpu_baseline": {"kind": "oracle", "cpu_model": cpu_model(), "results": cpu,
+                            "sample": "one row through each linear (the whole weight decoded), "
+                                      "repeated for 1 s, at all host threads and at one"},
            "note": "us: per call from HIP-graph replay of the calls (no host launch cost), each "
                    "call on a weight copy not in cache; eager_us: the same calls launched one by "
                    "one from Python; hot_us: graph replay of one copy called again and again "
@@ -696,7 +744,8 @@ def ccq_encode(args):
         oracle.quantize(sample, oracle.CCQ, refine=True)
         dt = time.perf_counter() - t1
         cpu = {"value": round(rows * k / dt / 1e6, 3), "unit": "M weights/s",
-               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "cpu_model": cpu_model(),
+            "kind": "oracle",
                "sample": f"{rows} rows x {k} of expert 0, refine on, {dt:.1f} s"}
     log(f"encode {ms:.1f} ms for {weights / 1e9:.2f} G weights ({weights / (ms * 1e-3) / 1e9:.1f} G weights/s), "
         f"{tf:.1f} fp64 TFLOP/s")
